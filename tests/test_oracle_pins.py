@@ -1,0 +1,11 @@
+"""The CPU oracle against its pins (library routines, brute force, exact
+arithmetic, closed forms and invariants); see tests/oracle_pins.py."""
+import pytest
+
+import oracle
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)
