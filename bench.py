@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE finalize hot path on one MI355X.
+
+A step is one launch of the fused finalize over one batch of synthetic input
+resident in HBM.  The default workload is the prefill finalize+RMSNorm
+(8192 tokens, hidden 4096, top-k 8, FP32 weights, 65536 gathered rows grouped
+by expert with Zipf(1.1) load over 256 experts).  To keep the gathered rows
+from being served by the 256 MB Infinity Cache, steps rotate over several
+device copies of the row matrix and output (at least 1.5 GiB in total), so
+every step reads its rows from HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config prefill]
+
+Prints one JSON line on stdout (diagnostics go to stderr): tokens/s over the
+timed region, the dominant kernel's achieved HBM bandwidth against the
+8 TB/s peak (HIP events around every launch, on the launch stream), and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+ROTATE_MIN_BYTES = 3 << 29          # 1.5 GiB of rotated rows + outputs
+KERNEL_SOURCES = ["moe_expert_output_finalize_amd/csrc/finalize_kernels.hip",
+                  "moe_expert_output_finalize_amd/csrc/capi.hip",
+                  "moe_expert_output_finalize_amd/csrc/launch.hpp"]
+
+WORKLOADS = {
+    "prefill": "prefill finalize+RMSNorm: 8192 tokens, hidden 4096, top-k 8, FP32 weights, "
+               "65536 rows grouped by expert (Zipf 1.1 over 256 experts)",
+    "decode": "decode finalize+RMSNorm: 256 tokens, hidden 4096 (row stride 4160), top-k 8, "
+              "BF16 weights, 2% invalid slots, weight before norm",
+    "tiny": "tiny finalize+RMSNorm: 16 tokens, hidden 4096, top-k 8, 5% invalid slots",
+    "beam4": "token-major finalize, no norm: 3000 live of 4096, top-k 8, hidden 7168, scale 2.5",
+    "beam5": "token-major finalize + post RMSNorm: 16000 live of 16384, top-k 16, hidden 2048",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="prefill", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time spent on the oracle sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run a plain device copy of this size (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        log(f"bench: {path} was measured on other kernel sources; traffic = null")
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------ workloads -----
+
+def index_map_bytes(c, norm: bool) -> int:
+    valid = int(((c.idx >= 0) & (c.idx < c.num_rows)).sum())
+    wbytes = 4 if c.weights_dtype == "fp32" else 2
+    T, K, H = c.num_tokens, c.top_k, c.hidden
+    return valid * H * 2 + T * H * 2 + T * K * 4 + T * K * wbytes + (H * 2 if norm else 0)
+
+
+def token_major_bytes(c) -> int:
+    L, K, H = c.live_tokens, c.top_k, c.hidden
+    return L * K * H * 2 + L * H * 2 + L * K * 4 + (H * 2 if c.post_weight is not None else 0)
+
+
+class IndexMapBench:
+    def __init__(self, c, torch, mf):
+        import numpy as np
+        self.c, self.torch, self.mf = c, torch, mf
+        dev = torch.device("cuda:0")
+        self.tokens = c.num_tokens
+        self.bytes = index_map_bytes(c, norm=True)
+        per_set = c.num_rows * c.row_stride * 2 + c.num_tokens * c.hidden * 2
+        self.sets = max(2, math.ceil(ROTATE_MIN_BYTES / per_set))
+        g = torch.from_numpy(c.gemm2.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.rows = [g] + [g.clone() for _ in range(self.sets - 1)]
+        self.outs = [torch.empty((c.num_tokens, c.hidden), dtype=torch.bfloat16, device=dev)
+                     for _ in range(self.sets)]
+        w = c.expert_weights
+        self.w = (torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+                  if w.dtype == np.uint16 else torch.from_numpy(w)).to(dev)
+        self.idx = torch.from_numpy(c.idx).to(dev)
+        self.nw = torch.from_numpy(c.norm_weight.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def step(self, i: int):
+        s = i % self.sets
+        c = self.c
+        self.mf.moe_finalize_rmsnorm(self.rows[s], self.w, self.idx, self.nw, self.outs[s],
+                                     eps=c.eps, gain_center=c.gain_center,
+                                     weight_before_norm=c.weight_before_norm)
+
+    def cpu_oracle(self, oracle, tokens: slice):
+        c = self.c
+        oracle.moe_finalize_rmsnorm(c.gemm2, c.expert_weights[tokens], c.idx[tokens],
+                                    c.norm_weight, eps=c.eps, gain_center=c.gain_center,
+                                    weight_before_norm=c.weight_before_norm)
+
+
+class TokenMajorBench:
+    def __init__(self, c, torch, mf):
+        import numpy as np
+        self.c, self.torch, self.mf = c, torch, mf
+        dev = torch.device("cuda:0")
+        self.tokens = c.live_tokens
+        self.bytes = token_major_bytes(c)
+        per_set = c.expert_outputs.nbytes + c.live_tokens * c.hidden * 2
+        self.sets = max(2, math.ceil(ROTATE_MIN_BYTES / per_set))
+        e = torch.from_numpy(c.expert_outputs.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.rows = [e] + [e.clone() for _ in range(self.sets - 1)]
+        self.outs = [torch.empty((c.live_tokens, c.hidden), dtype=torch.bfloat16, device=dev)
+                     for _ in range(self.sets)]
+        self.w = torch.from_numpy(c.expert_weights).to(dev)
+        self.pw = (None if c.post_weight is None else
+                   torch.from_numpy(c.post_weight.view(np.int16)).view(torch.bfloat16).to(dev))
+
+    def step(self, i: int):
+        s = i % self.sets
+        c = self.c
+        self.mf.beam_moe_finalize(self.rows[s], self.w, self.outs[s], c.routed_scale, self.pw,
+                                  c.post_eps)
+
+    def cpu_oracle(self, oracle, tokens: slice):
+        c = self.c
+        n = len(range(*tokens.indices(c.live_tokens)))
+        oracle.beam_moe_finalize(c.expert_outputs[tokens], c.expert_weights[tokens], n,
+                                 c.routed_scale, c.post_weight, c.post_eps)
+
+
+def cpu_baseline(bench, seconds: float) -> dict:
+    """The oracle (single-threaded C) on whole passes over the workload's
+    tokens, repeated until `seconds` of CPU time have been spent."""
+    import oracle
+    oracle.build()
+    T = bench.tokens
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        bench.cpu_oracle(oracle, slice(0, T))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full pass(es) over all {T} tokens of the same workload, "
+                      f"single thread, {el:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def copy_ceiling(torch, mib: int = 1024, reps: int = 10) -> float:
+    """GB/s (read + write) of a plain device-to-device copy."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the finalize runs on one GPU's share of the tokens; see DESIGN.md for "
+              "how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_probe_mib:
+        log(f"bench: copy probe of {args.copy_probe_mib} MiB")
+        gbps = copy_ceiling(torch, args.copy_probe_mib, reps=5)
+        print(json.dumps({"copy_probe_mib": args.copy_probe_mib, "GBps": gbps}))
+        return
+
+    import moe_expert_output_finalize_amd as mf
+    import workloads as wl
+
+    log(f"bench: generating the {args.config} workload")
+    c = wl.CONFIGS[args.config]()
+    bench = (IndexMapBench if isinstance(c, wl.IndexMapCase) else TokenMajorBench)(c, torch, mf)
+    log(f"bench: {bench.sets} rotating buffer sets, {bench.bytes} algorithmic bytes/step")
+
+    for i in range(args.warmup):
+        bench.step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record()
+        bench.step(args.warmup + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = sum(kern_ms) / K * 1e-3
+    kern_sorted = sorted(kern_ms)
+
+    achieved = bench.bytes / kern_avg_s / 1e9
+    traffic = stored_traffic(args.config)
+    ceiling = copy_ceiling(torch)
+    log(f"bench: kernel avg {kern_avg_s * 1e6:.2f} us (min {kern_sorted[0] * 1e3:.2f}, "
+        f"median {kern_sorted[K // 2] * 1e3:.2f}), {achieved:.0f} GB/s; "
+        f"copy ceiling {ceiling:.0f} GB/s; wall {wall * 1e3 / K:.2f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle for >= {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(bench, args.cpu_seconds)
+
+    config = {"workload": WORKLOADS[args.config], "name": args.config,
+              "tokens_per_step": bench.tokens, "algorithmic_bytes_per_step": bench.bytes,
+              "rotating_buffer_sets": bench.sets, "io_dtype": "bf16"}
+    if isinstance(c, wl.IndexMapCase):
+        config.update(hidden=c.hidden, top_k=c.top_k, num_rows=c.num_rows,
+                      row_stride=c.row_stride, weights=c.weights_dtype)
+    else:
+        config.update(hidden=c.hidden, top_k=c.top_k, capacity=c.capacity)
+    rec = {
+        "metric": "tokens/sec and achieved HBM GB/s (% of peak), finalize+RMSNorm h=4096 k=8",
+        "value": bench.tokens * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": config,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic, "kernel_avg_us": kern_avg_s * 1e6,
+                     "kernel_median_us": kern_sorted[K // 2] * 1e3,
+                     "copy_ceiling_GBps": ceiling},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

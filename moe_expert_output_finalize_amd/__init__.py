@@ -1,0 +1,185 @@
+"""MoE expert-output finalize for MI355X (gfx950): Python binding.
+
+Thin ctypes layer over ``libmoe_finalize.so`` (C ABI in
+``include/moe_finalize.h``).  It only marshals torch tensors into pointers,
+sizes and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is not built,
+importing this package raises.
+
+Entry points (same names as the C ABI):
+  moe_finalize_rmsnorm  index-map finalize + per-token RMSNorm
+                        (FlashInfer "flashinfer.comm.tp_moe_finalize_rmsnorm")
+  moe_finalize          index-map finalize without a norm
+  beam_moe_finalize     token-major finalize with BF16 rounding points and an
+                        optional RMSNorm (vLLM "vllm.models.beam.nvidia.moe_finalize")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_finalize.so")
+
+MF_OK = 0
+MF_DTYPE_BF16 = 1
+MF_DTYPE_FP32 = 2
+
+__all__ = ["moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "FinalizeError",
+           "lib", "LIB_PATH"]
+
+
+class FinalizeError(ValueError):
+    """A finalize entry point rejected its arguments or failed to launch."""
+
+    def __init__(self, name: str, status: int, message: str):
+        super().__init__(f"{name}: {message} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with "
+            "`python -m moe_expert_output_finalize_amd.build` (or __graft_entry__.build())")
+    so = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    so.moe_finalize_rmsnorm.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, i64, i32, i32,
+                                        f32, f32, i32, vp]
+    so.moe_finalize.argtypes = [vp, i64, i64, vp, i32, vp, vp, i64, i32, i32, vp]
+    so.beam_moe_finalize.argtypes = [vp, i64, i32, i32, vp, i64, vp, i64, vp, f32, f32, i32, vp]
+    for f in (so.moe_finalize_rmsnorm, so.moe_finalize, so.beam_moe_finalize):
+        f.restype = i32
+    so.mf_status_string.argtypes = [ctypes.c_int]
+    so.mf_status_string.restype = ctypes.c_char_p
+    so.mf_last_error_message.argtypes = []
+    so.mf_last_error_message.restype = ctypes.c_char_p
+    return so
+
+
+lib = _load()
+
+
+def _raise_on(name: str, rc: int) -> None:
+    if rc != MF_OK:
+        msg = lib.mf_status_string(rc).decode()
+        extra = lib.mf_last_error_message().decode()
+        raise FinalizeError(name, rc, msg + (f": {extra}" if extra else ""))
+
+
+def _stream(stream, device) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require(cond: bool, name: str, what: str) -> None:
+    if not cond:
+        raise ValueError(f"{name}: {what}")
+
+
+def _check_device(name: str, *tensors) -> torch.device:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        _require(t.is_cuda, name, "tensors must be on a GPU")
+        dev = t.device if dev is None else dev
+        _require(t.device == dev, name, "tensors must be on one device")
+    return dev
+
+
+def _weights_dtype(name: str, w: torch.Tensor) -> int:
+    if w.dtype == torch.bfloat16:
+        return MF_DTYPE_BF16
+    if w.dtype == torch.float32:
+        return MF_DTYPE_FP32
+    raise ValueError(f"{name}: expert_weights must be bfloat16 or float32")
+
+
+def _index_map_args(name, gemm2_permuted, expert_weights, idx, output):
+    _require(gemm2_permuted.dim() == 2 and gemm2_permuted.dtype == torch.bfloat16, name,
+             "gemm2_permuted must be a 2-D bfloat16 tensor")
+    _require(gemm2_permuted.stride(1) == 1 or gemm2_permuted.shape[1] <= 1, name,
+             "gemm2_permuted must have a unit-stride last dimension")
+    _require(idx.dim() == 2 and idx.dtype == torch.int32 and idx.is_contiguous(), name,
+             "expanded_idx_to_permuted_idx must be a contiguous int32 [tokens, top_k] tensor")
+    _require(expert_weights.shape == idx.shape and expert_weights.is_contiguous(), name,
+             "expert_weights must be contiguous with the index map's shape")
+    _require(output.dim() == 2 and output.dtype == torch.bfloat16 and output.is_contiguous(),
+             name, "output must be a contiguous bfloat16 [tokens, hidden] tensor")
+    _require(output.shape[0] == idx.shape[0], name, "output and index map disagree on tokens")
+    _require(gemm2_permuted.shape[1] >= output.shape[1], name,
+             "gemm2_permuted is narrower than hidden")
+    row_stride = gemm2_permuted.stride(0) if gemm2_permuted.shape[0] > 1 else gemm2_permuted.shape[1]
+    return (gemm2_permuted.data_ptr(), gemm2_permuted.shape[0], row_stride,
+            expert_weights.data_ptr(), _weights_dtype(name, expert_weights), idx.data_ptr())
+
+
+def moe_finalize_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
+                         expanded_idx_to_permuted_idx: torch.Tensor, norm_weight: torch.Tensor,
+                         output: torch.Tensor, *, eps: float, gain_center: float,
+                         weight_before_norm: bool, stream=None) -> None:
+    """Index-map finalize fused with per-token RMSNorm, written into ``output``."""
+    name = "moe_finalize_rmsnorm"
+    dev = _check_device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
+                        norm_weight, output)
+    g, rows, stride, w, wdt, idx = _index_map_args(name, gemm2_permuted, expert_weights,
+                                                    expanded_idx_to_permuted_idx, output)
+    _require(norm_weight.dim() == 1 and norm_weight.dtype == torch.bfloat16 and
+             norm_weight.is_contiguous() and norm_weight.shape[0] == output.shape[1], name,
+             "norm_weight must be a contiguous bfloat16 [hidden] tensor")
+    T, K = expanded_idx_to_permuted_idx.shape
+    rc = lib.moe_finalize_rmsnorm(g, rows, stride, w, wdt, idx, norm_weight.data_ptr(),
+                                  output.data_ptr(), T, output.shape[1], K, float(eps),
+                                  float(gain_center), int(bool(weight_before_norm)),
+                                  _stream(stream, dev))
+    _raise_on(name, rc)
+
+
+def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
+                 expanded_idx_to_permuted_idx: torch.Tensor, output: torch.Tensor,
+                 stream=None) -> None:
+    """Index-map finalize without a norm: output = bf16(FP32 routed sum)."""
+    name = "moe_finalize"
+    dev = _check_device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
+                        output)
+    g, rows, stride, w, wdt, idx = _index_map_args(name, gemm2_permuted, expert_weights,
+                                                    expanded_idx_to_permuted_idx, output)
+    T, K = expanded_idx_to_permuted_idx.shape
+    rc = lib.moe_finalize(g, rows, stride, w, wdt, idx, output.data_ptr(), T, output.shape[1],
+                          K, _stream(stream, dev))
+    _raise_on(name, rc)
+
+
+def beam_moe_finalize(expert_outputs: torch.Tensor, expert_weights: torch.Tensor,
+                      output: torch.Tensor, routed_scale: float = 1.0,
+                      post_weight: torch.Tensor | None = None, post_eps: float | None = None,
+                      stream=None) -> torch.Tensor:
+    """Token-major finalize of output.shape[0] live rows; returns ``output``."""
+    name = "beam_moe_finalize"
+    dev = _check_device(name, expert_outputs, expert_weights, output, post_weight)
+    _require(expert_outputs.dim() == 3 and expert_weights.dim() == 2 and output.dim() == 2,
+             name, "expected [capacity, top_k, hidden], [rows, top_k] and [live, hidden]")
+    capacity, top_k, hidden = expert_outputs.shape
+    _require(expert_outputs.dtype == torch.bfloat16 and output.dtype == torch.bfloat16, name,
+             "expert_outputs and output must be bfloat16")
+    _require(expert_weights.dtype == torch.float32, name, "expert_weights must be float32")
+    for t in (expert_outputs, expert_weights, output):
+        _require(t.is_contiguous(), name, "tensors must be contiguous")
+    _require(output.shape[1] == hidden and expert_weights.shape[1] == top_k, name,
+             "hidden / top_k mismatch")
+    if post_weight is not None:
+        _require(post_eps is not None, name, "post_weight needs post_eps")
+        _require(post_weight.shape == (hidden,) and post_weight.dtype == torch.bfloat16 and
+                 post_weight.is_contiguous(), name,
+                 "post_weight must be a contiguous bfloat16 [hidden] tensor")
+    rc = lib.beam_moe_finalize(
+        expert_outputs.data_ptr(), capacity, top_k, hidden, expert_weights.data_ptr(),
+        expert_weights.shape[0], output.data_ptr(), output.shape[0],
+        None if post_weight is None else post_weight.data_ptr(), float(routed_scale),
+        float(post_eps or 0.0), int(post_eps is not None), _stream(stream, dev))
+    _raise_on(name, rc)
+    return output

@@ -1,0 +1,176 @@
+// C ABI of libmoe_finalize.so: argument validation and launch.
+//
+// Every check runs on the host before any HIP call, so a rejected call has
+// no side effect.  The checks are the C form of the parameter contracts on
+// the FlashInfer page "flashinfer.comm.tp_moe_finalize_rmsnorm" (Parameters:
+// shapes, dtypes, unit-stride rows with a row stride that is a multiple of 8
+// elements, 16-byte alignment, hidden 4096 and top-k 8) and of the argument
+// checks in beam_moe_finalize on the vLLM page
+// "vllm.models.beam.nvidia.moe_finalize" (1 <= top_k <= 32, hidden a
+// multiple of 256 in [256, 8192], live rows <= capacity, weight rows >= live
+// rows, post_weight only with a norm, nothing to do for zero live rows).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "launch.hpp"
+#include "moe_finalize.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool hidden_in_envelope(int32_t hidden) { return hidden >= 256 && hidden <= 8192 && hidden % 256 == 0; }
+
+int launch(const mf::FinalizeArgs &a, mf::Epilogue epi, void *stream)
+{
+    const hipError_t err = mf::launch_finalize(a, epi, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s (%d)",
+                 hipGetErrorString(err), static_cast<int>(err));
+        return MF_ERR_LAUNCH_FAILED;
+    }
+    g_last_error[0] = '\0';
+    return MF_OK;
+}
+
+// Checks shared by the two index-map entry points.  Returns MF_OK and fills
+// `a`, or an error status.
+int check_index_map(const void *gemm2_permuted, int64_t num_rows, int64_t row_stride,
+                    const void *expert_weights, int32_t weights_dtype, const int32_t *idx,
+                    void *output, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                    mf::FinalizeArgs &a)
+{
+    if (num_tokens < 0 || num_tokens > INT32_MAX || num_rows < 0)
+        return MF_ERR_BAD_SHAPE;
+    if (row_stride < hidden)
+        return MF_ERR_BAD_SHAPE;
+    if (weights_dtype != MF_DTYPE_BF16 && weights_dtype != MF_DTYPE_FP32)
+        return MF_ERR_BAD_DTYPE;
+    if (row_stride % 8 != 0)
+        return MF_ERR_MISALIGNED;
+    if (num_tokens > 0) {
+        if ((num_rows > 0 && !gemm2_permuted) || !expert_weights || !idx || !output)
+            return MF_ERR_NULL_POINTER;
+        if (!aligned(gemm2_permuted, 16) || !aligned(expert_weights, 16) || !aligned(idx, 16) ||
+            !aligned(output, 16))
+            return MF_ERR_MISALIGNED;
+    }
+    a = mf::FinalizeArgs{};
+    a.rows = static_cast<const uint16_t *>(gemm2_permuted);
+    a.row_stride = row_stride;
+    a.num_rows = num_rows;
+    a.idx = idx;
+    a.weights = expert_weights;
+    a.weights_bf16 = weights_dtype == MF_DTYPE_BF16;
+    a.out = static_cast<uint16_t *>(output);
+    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.hidden = hidden;
+    a.top_k = top_k;
+    return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_finalize_rmsnorm(const void *gemm2_permuted, int64_t num_rows, int64_t row_stride,
+                         const void *expert_weights, int32_t weights_dtype,
+                         const int32_t *expanded_idx_to_permuted_idx, const void *norm_weight,
+                         void *output, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                         float eps, float gain_center, int32_t weight_before_norm, void *stream)
+{
+    if (hidden != 4096 || top_k != 8)
+        return MF_ERR_BAD_SHAPE;
+    mf::FinalizeArgs a;
+    const int rc = check_index_map(gemm2_permuted, num_rows, row_stride, expert_weights,
+                                   weights_dtype, expanded_idx_to_permuted_idx, output,
+                                   num_tokens, hidden, top_k, a);
+    if (rc != MF_OK)
+        return rc;
+    if (num_tokens == 0)
+        return MF_OK;
+    if (!norm_weight)
+        return MF_ERR_NULL_POINTER;
+    if (!aligned(norm_weight, 16))
+        return MF_ERR_MISALIGNED;
+    a.gain = static_cast<const uint16_t *>(norm_weight);
+    a.eps = eps;
+    a.gain_center = gain_center;
+    return launch(a, weight_before_norm ? mf::Epilogue::kRmsNormWeightFirst : mf::Epilogue::kRmsNorm,
+                  stream);
+}
+
+int moe_finalize(const void *gemm2_permuted, int64_t num_rows, int64_t row_stride,
+                 const void *expert_weights, int32_t weights_dtype,
+                 const int32_t *expanded_idx_to_permuted_idx, void *output, int64_t num_tokens,
+                 int32_t hidden, int32_t top_k, void *stream)
+{
+    if (!hidden_in_envelope(hidden) || top_k < 1 || top_k > 32)
+        return MF_ERR_BAD_SHAPE;
+    mf::FinalizeArgs a;
+    const int rc = check_index_map(gemm2_permuted, num_rows, row_stride, expert_weights,
+                                   weights_dtype, expanded_idx_to_permuted_idx, output,
+                                   num_tokens, hidden, top_k, a);
+    if (rc != MF_OK)
+        return rc;
+    if (num_tokens == 0)
+        return MF_OK;
+    return launch(a, mf::Epilogue::kRound, stream);
+}
+
+int beam_moe_finalize(const void *expert_outputs, int64_t capacity, int32_t top_k, int32_t hidden,
+                      const float *expert_weights, int64_t weight_rows, void *output,
+                      int64_t live_tokens, const void *post_weight, float routed_scale,
+                      float post_eps, int32_t has_norm, void *stream)
+{
+    if (top_k < 1 || top_k > 32 || !hidden_in_envelope(hidden))
+        return MF_ERR_BAD_SHAPE;
+    if (capacity < 0 || live_tokens < 0 || live_tokens > capacity || live_tokens > INT32_MAX ||
+        weight_rows < live_tokens)
+        return MF_ERR_BAD_SHAPE;
+    if (post_weight && !has_norm)
+        return MF_ERR_BAD_ARGUMENT;
+    if (live_tokens == 0)
+        return MF_OK;
+    if (!expert_outputs || !expert_weights || !output)
+        return MF_ERR_NULL_POINTER;
+    if (!aligned(expert_outputs, 16) || !aligned(expert_weights, 4) || !aligned(output, 16) ||
+        !aligned(post_weight, 16))
+        return MF_ERR_MISALIGNED;
+    mf::FinalizeArgs a{};
+    a.rows = static_cast<const uint16_t *>(expert_outputs);
+    a.row_stride = hidden;
+    a.num_rows = capacity * top_k;
+    a.idx = nullptr;
+    a.weights = expert_weights;
+    a.weights_bf16 = false;
+    a.gain = static_cast<const uint16_t *>(post_weight);
+    a.out = static_cast<uint16_t *>(output);
+    a.num_tokens = static_cast<int32_t>(live_tokens);
+    a.hidden = hidden;
+    a.top_k = top_k;
+    a.eps = post_eps;
+    a.routed_scale = routed_scale;
+    return launch(a, has_norm ? mf::Epilogue::kBeamNorm : mf::Epilogue::kBeam, stream);
+}
+
+const char *mf_status_string(int status)
+{
+    switch (status) {
+    case MF_OK: return "ok";
+    case MF_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MF_ERR_BAD_SHAPE: return "a size is negative, inconsistent or outside the supported envelope";
+    case MF_ERR_BAD_DTYPE: return "unsupported weights dtype";
+    case MF_ERR_MISALIGNED: return "a pointer or row stride is not 16-byte aligned";
+    case MF_ERR_BAD_ARGUMENT: return "inconsistent optional arguments (post_weight without a norm)";
+    case MF_ERR_LAUNCH_FAILED: return "the HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *mf_last_error_message(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,397 @@
+// gfx950 kernels for the MoE expert-output finalize.
+//
+// What is computed (sources are web pages, cited by title and section):
+//  - FlashInfer "flashinfer.comm.tp_moe_finalize_rmsnorm", description and
+//    Parameters: per token, gather the rows an index map selects (an index
+//    outside [0, num_rows) contributes nothing), sum them weighted by the
+//    routing weights in FP32, then RMSNorm with eps inside the root and an
+//    effective weight norm_weight + gain_center (FP32), applied either to the
+//    sum before the statistics or to the normalised value.
+//  - vLLM "vllm.models.beam.nvidia.moe_finalize", beam_moe_finalize: the same
+//    reduction over token-major rows [t, k, :], rounded to BF16, multiplied by
+//    routed_scale and rounded to BF16 again before an optional RMSNorm.
+//
+// Mapping onto CDNA4.  The path moves ~70 KB per token and does ~1 FP32 op
+// per byte, so it is bound by HBM bandwidth and uses no matrix cores:
+//  - one workgroup per token; hidden/8 threads-or-fewer each own VPT 16-byte
+//    column vectors of the token (vector j = lane + i * blockDim), so every
+//    wave reads 1 KiB contiguous runs of each gathered row;
+//  - the token's indices and weights are uniform, so they live in SGPRs and
+//    validity is a scalar branch: invalid slots issue no memory traffic;
+//  - all of a token's row vectors (top-k 8 or 16) or batches of 16 vectors
+//    per thread are in flight before the first FMA;
+//  - the FP32 sum, the sum of squares and the normalised values stay in
+//    VGPRs; the cross-lane sum uses DPP row operations, the cross-wave sum
+//    one LDS exchange and barrier;
+//  - BF16 rounding is the CDNA4 packed convert (nearest even), two values
+//    per instruction, and results leave as 16-byte stores;
+//  - workgroups are numbered so that each XCD (dispatched round-robin) works
+//    on a contiguous block of tokens.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+#ifndef MF_NONTEMPORAL_ROWS
+#define MF_NONTEMPORAL_ROWS 1   // gathered rows are read exactly once
+#endif
+#ifndef MF_NONTEMPORAL_OUT
+#define MF_NONTEMPORAL_OUT 1    // output rows are written exactly once
+#endif
+#ifndef MF_XCD_REMAP
+#define MF_XCD_REMAP 1
+#endif
+
+namespace mf {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 16;
+constexpr uint32_t kNumXcd = 8;
+
+// ------------------------------------------------------------ BF16 -------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Element e (0..7) of a 16-byte vector of BF16 values, widened exactly.
+__device__ __forceinline__ float elem(const u32x4 &v, int e)
+{
+    const uint32_t u = v[e >> 1];
+    return (e & 1) ? bf16_hi(u) : bf16_lo(u);
+}
+
+// Round two FP32 values to BF16 (nearest, ties to even) and pack them, the
+// first in the low half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ------------------------------------------------------------ memory -----
+
+__device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
+{
+#if MF_NONTEMPORAL_ROWS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void store_out_vec(u32x4 *p, const u32x4 &v)
+{
+#if MF_NONTEMPORAL_OUT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_weight(const void *w, int64_t i)
+{
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(w)[i] << 16);
+    else
+        return static_cast<const float *>(w)[i];
+}
+
+// ------------------------------------------------------------ reduction --
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of v over the workgroup, returned to every thread.  All threads of the
+// workgroup must call it (it contains a barrier when there are several waves).
+__device__ __forceinline__ float block_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror: 8-lane sums
+    v += dpp_mov<0x140>(v);   // row_mirror: 16-lane sums
+    const int iv = __builtin_bit_cast(int, v);
+    float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)) +
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+    const int waves = blockDim.x / kWave;
+    if (waves == 1)
+        return s;
+    __shared__ float part[kMaxWaves];
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        part[threadIdx.x / kWave] = s;
+    __syncthreads();
+    s = 0.0f;
+    for (int i = 0; i < waves; ++i)
+        s += part[i];
+    return s;
+}
+
+// Token handled by this workgroup.  Consecutive workgroup ids go to the
+// XCDs in turn, so id b runs on XCD b % 8; give XCD x the x-th contiguous
+// range of tokens.  A bijection on [0, G) for any G.
+__device__ __forceinline__ int64_t token_of_block()
+{
+    const uint32_t b = blockIdx.x;
+#if MF_XCD_REMAP
+    const uint32_t G = gridDim.x;
+    const uint32_t per = G / kNumXcd, rem = G % kNumXcd;
+    const uint32_t x = b % kNumXcd, r = b / kNumXcd;
+    return (int64_t)(x * per + (x < rem ? x : rem) + r);
+#else
+    return (int64_t)b;
+#endif
+}
+
+// ------------------------------------------------------------ kernel -----
+
+// LAYOUT_IDX: rows come through the index map (else token major).
+// KC: top_k when known at compile time (0: read a.top_k).
+// VPT: 16-byte vectors per thread; EXACT: hidden/8 == blockDim.x * VPT.
+template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
+__global__ void __launch_bounds__(VPT == 1 ? 1024 : 512)
+finalize_kernel(const FinalizeArgs a)
+{
+    // Slots whose rows are in flight together: all of them for the
+    // compile-time slot counts, else batches of 16 / VPT.
+    constexpr int KB = KC > 0 ? KC : 16 / VPT;
+    constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
+                           EPI == Epilogue::kBeamNorm;
+    const int top_k = KC > 0 ? KC : a.top_k;
+    const int team = blockDim.x;
+    const int lane = threadIdx.x;
+    const int nv = a.hidden >> 3;
+    const int64_t t = token_of_block();
+    const int64_t tk = t * top_k;
+
+    // The norm weight is shared by every token and stays cache resident;
+    // fetch it first so its latency hides under the gather.
+    u32x4 gv[VPT];
+    if constexpr (kNorm) {
+        const bool have = EPI != Epilogue::kBeamNorm || a.gain != nullptr;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int j = lane + i * team;
+            gv[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (have && (EXACT || j < nv))
+                gv[i] = reinterpret_cast<const u32x4 *>(a.gain)[j];
+        }
+    }
+
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[i][e] = 0.0f;
+
+    for (int k0 = 0; k0 < top_k; k0 += KB) {
+        // Uniform per-slot data first (scalar loads, one wait), then every
+        // valid slot's row vectors, then the FMAs in ascending slot order.
+        int64_t row_off[KB];   // elements
+        bool ok[KB];
+        float w[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const int k = k0 + b;
+            const bool live = KC > 0 || k < top_k;
+            ok[b] = false;
+            w[b] = 0.0f;
+            row_off[b] = 0;
+            if (live) {
+                w[b] = load_weight<W_BF16>(a.weights, tk + k);
+                if constexpr (LAYOUT_IDX) {
+                    const int32_t i = a.idx[tk + k];
+                    ok[b] = i >= 0 && (int64_t)i < a.num_rows;
+                    row_off[b] = (int64_t)i * a.row_stride;
+                } else {
+                    ok[b] = true;
+                    row_off[b] = (tk + k) * (int64_t)a.hidden;
+                }
+            }
+        }
+        u32x4 v[KB][VPT];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (ok[b]) {
+                const u32x4 *r = reinterpret_cast<const u32x4 *>(a.rows + row_off[b]);
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int j = lane + i * team;
+                    if (EXACT || j < nv)
+                        v[b][i] = load_row_vec(r + j);
+                    else
+                        v[b][i] = (u32x4){0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (ok[b]) {
+#pragma unroll
+                for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
+            }
+        }
+    }
+
+    uint16_t *out_row = a.out + t * (int64_t)a.hidden;
+    auto store = [&](int i, const u32x4 &o) {
+        const int j = lane + i * team;
+        if (EXACT || j < nv)
+            store_out_vec(reinterpret_cast<u32x4 *>(out_row) + j, o);
+    };
+
+    if constexpr (EPI == Epilogue::kRound) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+            store(i, o);
+        }
+        return;
+    }
+
+    if constexpr (EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm) {
+        // r = bf16(acc); s = bf16(r * routed_scale); s is kept widened in acc.
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t r = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+                const uint32_t s = pack_bf16x2(bf16_lo(r) * a.routed_scale,
+                                               bf16_hi(r) * a.routed_scale);
+                o[q] = s;
+                acc[i][2 * q] = bf16_lo(s);
+                acc[i][2 * q + 1] = bf16_hi(s);
+            }
+            if constexpr (EPI == Epilogue::kBeam)
+                store(i, o);
+        }
+        if constexpr (EPI == Epilogue::kBeam)
+            return;
+    }
+
+    if constexpr (kNorm) {
+        // Effective per-element weight.
+        float g[VPT][8];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (EPI == Epilogue::kBeamNorm)
+                    g[i][e] = a.gain ? elem(gv[i], e) : 1.0f;
+                else
+                    g[i][e] = elem(gv[i], e) + a.gain_center;
+            }
+        if constexpr (EPI == Epilogue::kRmsNormWeightFirst) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[i][e] *= g[i][e];
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);   // idle vectors hold 0
+        ss = block_sum(ss);
+        const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                y[e] = acc[i][e] * inv;
+                if constexpr (EPI != Epilogue::kRmsNormWeightFirst)
+                    y[e] *= g[i][e];
+            }
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_bf16x2(y[2 * q], y[2 * q + 1]);
+            store(i, o);
+        }
+    }
+}
+
+// ------------------------------------------------------------ dispatch ---
+
+template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI, int KC>
+hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
+{
+    // hidden = 256 n.  n % 4 == 0: 2 vectors per thread, 16 n threads;
+    // n even: 1 vector, 32 n threads; n odd: 1 vector, 32 (n + 1) threads
+    // with the last half wave idle.
+    const int n = a.hidden / 256;
+    const dim3 grid((unsigned)a.num_tokens);
+    if (n % 4 == 0)
+        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 2, true>), grid,
+                           dim3(16 * n), 0, s, a);
+    else if (n % 2 == 0)
+        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 1, true>), grid,
+                           dim3(32 * n), 0, s, a);
+    else
+        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 1, false>), grid,
+                           dim3(32 * (n + 1)), 0, s, a);
+    return hipGetLastError();
+}
+
+// Compile-time slot counts for the common top-k values, runtime otherwise.
+template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI>
+hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
+{
+    switch (a.top_k) {
+    case 8:
+        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 8>(a, s);
+    case 16:
+        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 16>(a, s);
+    default:
+        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 0>(a, s);
+    }
+}
+
+template <Epilogue EPI>
+hipError_t launch_index_map(const FinalizeArgs &a, hipStream_t s)
+{
+    return a.weights_bf16 ? launch_topk<true, true, EPI>(a, s)
+                          : launch_topk<true, false, EPI>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const FinalizeArgs &a, Epilogue epi, hipStream_t s)
+{
+    switch (epi) {
+    case Epilogue::kRound:
+        return launch_index_map<Epilogue::kRound>(a, s);
+    case Epilogue::kRmsNorm:
+        return launch_index_map<Epilogue::kRmsNorm>(a, s);
+    case Epilogue::kRmsNormWeightFirst:
+        return launch_index_map<Epilogue::kRmsNormWeightFirst>(a, s);
+    case Epilogue::kBeam:
+        return launch_topk<false, false, Epilogue::kBeam>(a, s);
+    case Epilogue::kBeamNorm:
+        return launch_topk<false, false, Epilogue::kBeamNorm>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mf

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle,
+element by element, on the same seeded inputs.
+
+Bar: outputs without a norm (moe_finalize, beam_moe_finalize without
+post-norm) are bit-exact, index masking included; normalised outputs are
+within 1 BF16 ulp of the oracle's single rounding of the exact result.
+Padding columns, rows past num_rows and rows of dead tokens hold NaN, so any
+read the method does not make shows up as NaN in the output.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_output_finalize_amd as mf
+import oracle
+import workloads as wl
+from gpu_util import IndexMapOnDevice, TokenMajorOnDevice, dev_bf16, host_bits
+from oracle_pins import _f32_probe_values, assert_bits_equal, assert_within_ulp
+
+pytestmark = pytest.mark.gpu
+
+NORM_MIN_EXACT = 0.98      # sanity floor on the bit-exact share of normalised outputs
+
+_cases = {}
+
+
+def case(name, make):
+    if name not in _cases:
+        _cases[name] = make()
+    return _cases[name]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------- runners ----
+
+def gpu_rmsnorm(d: IndexMapOnDevice, **kw) -> np.ndarray:
+    c = d.case
+    args = dict(eps=c.eps, gain_center=c.gain_center, weight_before_norm=c.weight_before_norm)
+    args.update(kw)
+    out = d.new_output()
+    mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, out, **args)
+    sync()
+    return host_bits(out)
+
+
+def oracle_rmsnorm(c: wl.IndexMapCase, **kw) -> np.ndarray:
+    args = dict(eps=c.eps, gain_center=c.gain_center, weight_before_norm=c.weight_before_norm)
+    args.update(kw)
+    return oracle.moe_finalize_rmsnorm(c.gemm2, c.expert_weights, c.idx, c.norm_weight, **args)
+
+
+def gpu_finalize(d: IndexMapOnDevice) -> np.ndarray:
+    out = d.new_output()
+    mf.moe_finalize(d.gemm2, d.weights, d.idx, out)
+    sync()
+    return host_bits(out)
+
+
+def oracle_finalize(c: wl.IndexMapCase) -> np.ndarray:
+    return oracle.moe_finalize(c.gemm2, c.expert_weights, c.idx, c.hidden)
+
+
+def gpu_beam(d: TokenMajorOnDevice, live=None) -> np.ndarray:
+    c = d.case
+    out = d.new_output(live)
+    mf.beam_moe_finalize(d.expert_outputs, d.weights, out, c.routed_scale, d.post_weight,
+                         c.post_eps)
+    sync()
+    return host_bits(out)
+
+
+def oracle_beam(c: wl.TokenMajorCase, live=None) -> np.ndarray:
+    live = c.live_tokens if live is None else live
+    return oracle.beam_moe_finalize(c.expert_outputs, c.expert_weights, live, c.routed_scale,
+                                    c.post_weight, c.post_eps)
+
+
+# ------------------------------------------------------ the five configs ----
+
+INDEX_CONFIGS = {
+    "tiny": lambda: wl.tiny(poison=True),
+    "tiny_nan_rows": lambda: wl.tiny(nan_rows_beyond=2),
+    "decode": lambda: wl.decode(poison=True),
+    "prefill": lambda: wl.prefill(),
+}
+
+
+@pytest.mark.parametrize("name", list(INDEX_CONFIGS))
+def test_rmsnorm_config(name):
+    c = case(name, INDEX_CONFIGS[name])
+    d = IndexMapOnDevice(c)
+    got = gpu_rmsnorm(d)
+    want = oracle_rmsnorm(c)
+    assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"{name} rmsnorm")
+    # the other weight placement and weight dtype on the same inputs
+    got = gpu_rmsnorm(d, weight_before_norm=not c.weight_before_norm)
+    want = oracle_rmsnorm(c, weight_before_norm=not c.weight_before_norm)
+    assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"{name} rmsnorm flipped placement")
+
+
+@pytest.mark.parametrize("name", list(INDEX_CONFIGS))
+def test_finalize_config(name):
+    c = case(name, INDEX_CONFIGS[name])
+    d = IndexMapOnDevice(c)
+    assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"{name} finalize")
+
+
+def test_rmsnorm_weight_dtypes():
+    for wdt in ("fp32", "bf16"):
+        c = wl.tiny(num_tokens=40, num_rows=400, weights_dtype=wdt, invalid_frac=0.1,
+                    poison=True, nan_rows_beyond=3)
+        d = IndexMapOnDevice(c)
+        for wbn in (False, True):
+            for gc in (1.0, 0.0, -0.5):
+                got = gpu_rmsnorm(d, weight_before_norm=wbn, gain_center=gc)
+                want = oracle_rmsnorm(c, weight_before_norm=wbn, gain_center=gc)
+                assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"{wdt} wbn={wbn} gc={gc}")
+        assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"{wdt} finalize")
+
+
+BEAM_CONFIGS = {
+    "beam4": lambda: wl.beam4(poison_dead=True),
+    "beam5": lambda: wl.beam5(poison_dead=True),
+}
+
+
+@pytest.mark.parametrize("name", list(BEAM_CONFIGS))
+def test_beam_config(name):
+    c = case(name, BEAM_CONFIGS[name])
+    d = TokenMajorOnDevice(c)
+    got = gpu_beam(d)
+    want = oracle_beam(c)
+    if c.post_eps is None:
+        assert_bits_equal(got, want, name)
+    else:
+        assert_within_ulp(got, want, 1, NORM_MIN_EXACT, name)
+
+
+# ------------------------------------------------------- envelope sweeps ----
+
+SWEEP_H = [256, 768, 1280, 2048, 3840, 4096, 7168, 8192]
+SWEEP_K = [1, 3, 8, 16, 32]
+
+
+@pytest.mark.parametrize("hidden", SWEEP_H)
+def test_finalize_envelope(hidden):
+    for K in SWEEP_K:
+        for wdt in ("fp32", "bf16"):
+            T = 11
+            c = wl.make_index_map_case(1000 + hidden + K, num_tokens=T, hidden=hidden, top_k=K,
+                                       num_rows=T * K + 5, row_stride=hidden + 8 * (K % 3),
+                                       weights_dtype=wdt, invalid_frac=0.15, poison=True,
+                                       nan_rows_beyond=2)
+            d = IndexMapOnDevice(c)
+            assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"H={hidden} K={K} {wdt}")
+
+
+@pytest.mark.parametrize("hidden", SWEEP_H)
+def test_beam_envelope(hidden):
+    for K in SWEEP_K:
+        for norm, pw, scale in ((False, None, 1.75), (True, 0.05, 1.0), (True, None, 0.3)):
+            c = wl.make_token_major_case(2000 + hidden + K, capacity=13, top_k=K, hidden=hidden,
+                                         live_tokens=11, routed_scale=scale,
+                                         post_eps=1e-6 if norm else None, post_weight_std=pw,
+                                         poison_dead=True)
+            d = TokenMajorOnDevice(c)
+            got, want = gpu_beam(d), oracle_beam(c)
+            what = f"H={hidden} K={K} norm={norm} pw={pw}"
+            if norm:
+                assert_within_ulp(got, want, 1, NORM_MIN_EXACT, what)
+            else:
+                assert_bits_equal(got, want, what)
+
+
+# ------------------------------------------------------------ edge cases ----
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 13, 257])
+def test_ragged_token_counts(T):
+    c = wl.tiny(num_tokens=T, num_rows=8 * T + 3, invalid_frac=0.05, poison=True,
+                nan_rows_beyond=2)
+    d = IndexMapOnDevice(c)
+    assert_within_ulp(gpu_rmsnorm(d), oracle_rmsnorm(c), 1, NORM_MIN_EXACT, f"T={T}")
+    assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"T={T}")
+
+
+def test_all_invalid_tokens_and_empty_row_matrix():
+    c = wl.tiny(num_tokens=12, num_rows=96)
+    c.idx[3, :] = -1
+    c.idx[7, :] = 9999
+    d = IndexMapOnDevice(c)
+    got_n, got_f = gpu_rmsnorm(d), gpu_finalize(d)
+    assert_within_ulp(got_n, oracle_rmsnorm(c), 1, NORM_MIN_EXACT, "all-invalid rmsnorm")
+    assert_bits_equal(got_f, oracle_finalize(c), "all-invalid finalize")
+    for t in (3, 7):
+        assert np.all((got_n[t] & 0x7FFF) == 0) and np.all((got_f[t] & 0x7FFF) == 0)
+    # no rows at all: every index is out of range
+    empty = torch.empty((0, 4096), dtype=torch.bfloat16, device="cuda")
+    out = d.new_output()
+    mf.moe_finalize(empty, d.weights, d.idx, out)
+    out2 = d.new_output()
+    mf.moe_finalize_rmsnorm(empty, d.weights, d.idx, d.norm_weight, out2, eps=1e-6,
+                            gain_center=1.0, weight_before_norm=False)
+    sync()
+    assert np.all((host_bits(out) & 0x7FFF) == 0)
+    assert np.all((host_bits(out2) & 0x7FFF) == 0)
+
+
+def test_zero_rows_launch_nothing():
+    c = wl.tiny(num_tokens=4, num_rows=32)
+    d = IndexMapOnDevice(c)
+    out = d.new_output(0x1234)
+    idx0 = d.idx[:0]
+    w0 = d.weights[:0]
+    mf.moe_finalize(d.gemm2, w0, idx0, out[:0])
+    mf.moe_finalize_rmsnorm(d.gemm2, w0, idx0, d.norm_weight, out[:0], eps=1e-6,
+                            gain_center=1.0, weight_before_norm=False)
+    b = TokenMajorOnDevice(wl.make_token_major_case(5, capacity=4, top_k=2, hidden=256,
+                                                    live_tokens=0))
+    bout = b.new_output(0)
+    mf.beam_moe_finalize(b.expert_outputs, b.weights, bout)
+    sync()
+    assert np.all(host_bits(out) == 0x1234)
+
+
+def test_live_equals_capacity_and_partial_live():
+    c = wl.make_token_major_case(77, capacity=40, top_k=8, hidden=7168, live_tokens=40,
+                                 routed_scale=2.5)
+    d = TokenMajorOnDevice(c)
+    assert_bits_equal(gpu_beam(d), oracle_beam(c), "live == capacity")
+    assert_bits_equal(gpu_beam(d, 17), oracle_beam(c, 17), "live 17")
+
+
+def test_extreme_values_propagate_like_the_oracle():
+    """Overflow to infinity, NaN in a valid row and huge weights behave as the
+    oracle's IEEE arithmetic says (compared by NaN-ness and bits).  The norm
+    is compared only where its FP32 sum of squares cannot overflow: the
+    oracle keeps that sum in binary64."""
+    c = wl.tiny(num_tokens=8, num_rows=64, invalid_frac=0.0)
+    g = c.gemm2_storage
+    g[c.idx[0, 0]] = wl.to_bf16_bits(np.full(4096, 3e38, np.float32))
+    g[c.idx[0, 1]] = wl.to_bf16_bits(np.full(4096, 3e38, np.float32))
+    c.expert_weights[0, :2] = 1.0                     # 6e38 -> +inf
+    g[c.idx[1, 3], 100:200] = 0x7FC0                  # NaN in a valid row
+    c.expert_weights[2, 5] = np.float32(1e30)         # large finite weight
+    d = IndexMapOnDevice(c)
+    assert_bits_equal(gpu_finalize(d), oracle_finalize(c), "extreme finalize")
+    keep = [t for t in range(8) if t != 2]
+    assert_within_ulp(gpu_rmsnorm(d)[keep], oracle_rmsnorm(c)[keep], 1, NORM_MIN_EXACT,
+                      "extreme rmsnorm (NaN/inf rows)")
+
+
+def test_hardware_bf16_rounding_matches_round_to_nearest_even():
+    """K = 1 and rows of 1.0 make the output bf16(weight): the packed convert
+    is checked on ties, subnormals, overflow and NaN against the oracle's
+    rounding (pinned to torch's cast)."""
+    x = _f32_probe_values(np.random.Generator(np.random.PCG64(31)))
+    n = x.size
+    H = 256
+    e = np.full((n, 1, H), 0x3F80, np.uint16)
+    case_ = wl.TokenMajorCase(e, x.reshape(n, 1).astype(np.float32), n, 1.0, None, None)
+    d = TokenMajorOnDevice(case_)
+    got = gpu_beam(d)
+    want = oracle_beam(case_)
+    assert_bits_equal(got, want, "beam bf16(w)")
+    rows = np.full((1, H), 0x3F80, np.uint16)
+    im = wl.IndexMapCase(rows, 1, H, x.reshape(n, 1).astype(np.float32),
+                         np.zeros((n, 1), np.int32), np.zeros(H, np.uint16), 1e-6, 0.0, False)
+    assert_bits_equal(gpu_finalize(IndexMapOnDevice(im)), oracle_finalize(im), "finalize bf16(w)")
+
+
+def test_runs_on_the_given_stream():
+    c = wl.tiny(num_tokens=32, num_rows=256)
+    d = IndexMapOnDevice(c)
+    s = torch.cuda.Stream()
+    out = d.new_output()
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(s):
+        mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, out, eps=c.eps,
+                                gain_center=c.gain_center, weight_before_norm=False)
+    s.synchronize()
+    assert_within_ulp(host_bits(out), oracle_rmsnorm(c), 1, NORM_MIN_EXACT, "side stream")
