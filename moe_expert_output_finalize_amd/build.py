@@ -1,6 +1,6 @@
 """Build libmoe_finalize.so (gfx950) in-tree with hipcc.
 
-    python -m moe_expert_output_finalize_amd.build [-D MACRO=VALUE ...]
+    python moe_expert_output_finalize_amd/build.py [-o OUT] [-D MACRO=VALUE ...]
 """
 from __future__ import annotations
 
@@ -50,5 +50,10 @@ def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = Fals
 
 
 if __name__ == "__main__":
-    defs = [a[2:] if a.startswith("-D") else a for a in sys.argv[1:]]
-    print(build(defines=defs, verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libmoe_finalize.so for gfx950")
+    ap.add_argument("-o", "--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="extra preprocessor definition, e.g. -D MF_MAX_VECS=8")
+    ns = ap.parse_args()
+    print(build(out=ns.out, defines=ns.defines, verbose=True))
