@@ -13,8 +13,10 @@ every step reads its rows from HBM.
 
 Prints one JSON line on stdout (diagnostics go to stderr): tokens/s over the
 timed region, the dominant kernel's achieved HBM bandwidth against the
-8 TB/s peak (HIP events around every launch, on the launch stream), and the
-CPU oracle's throughput on a bounded sample of the same workload.
+8 TB/s peak (a pair of HIP events on the launch stream around the timed
+back-to-back launches), the fused kernel against the unfused two-kernel
+baseline, and the CPU oracle's throughput on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -128,6 +130,24 @@ class IndexMapBench:
                                      eps=c.eps, gain_center=c.gain_center,
                                      weight_before_norm=c.weight_before_norm)
 
+    # The unfused baseline: moe_finalize into a BF16 intermediate, then the
+    # standalone norm (two launches, one extra write and read of [T, H]).
+    def unfused_parts(self):
+        c, torch = self.c, self.torch
+        mids = [torch.empty_like(o) for o in self.outs]
+
+        def finalize(i):
+            s = i % self.sets
+            self.mf.moe_finalize(self.rows[s], self.w, self.idx, mids[s])
+
+        def norm(i):
+            s = i % self.sets
+            self.mf.mf_rmsnorm(mids[s], self.nw, self.outs[s], eps=c.eps,
+                               gain_center=c.gain_center,
+                               weight_before_norm=c.weight_before_norm)
+        extra = 2 * c.num_tokens * c.hidden * 2
+        return [("moe_finalize", finalize), ("mf_rmsnorm", norm)], self.bytes + extra
+
     def cpu_oracle(self, oracle, tokens: slice):
         c = self.c
         oracle.moe_finalize_rmsnorm(c.gemm2, c.expert_weights[tokens], c.idx[tokens],
@@ -163,6 +183,28 @@ class TokenMajorBench:
         n = len(range(*tokens.indices(c.live_tokens)))
         oracle.beam_moe_finalize(c.expert_outputs[tokens], c.expert_weights[tokens], n,
                                  c.routed_scale, c.post_weight, c.post_eps)
+
+
+def time_launches(torch, fns, steps: int, warmup: int):
+    """Per-launch HIP-event durations (us, mean over steps) of each function
+    in `fns` run back to back per step, and the wall time per step (ms)."""
+    for i in range(warmup):
+        for _, fn in fns:
+            fn(i)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for (s, e), (_, fn) in zip(ev[i], fns):
+            s.record()
+            fn(warmup + i)
+            e.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    us = {name: sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)) / steps * 1e3
+          for j, (name, _) in enumerate(fns)}
+    return us, wall_ms
 
 
 def cpu_baseline(bench, seconds: float) -> dict:
@@ -242,27 +284,38 @@ def main():
         bench.step(i)
     torch.cuda.synchronize()
 
+    # Timed region: K back-to-back launches on the current stream, bracketed
+    # by synchronisation (wall clock) and by one pair of HIP events recorded
+    # on that same stream (kernel time per launch = event span / K).
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_start.record()
     for i in range(K):
-        starts[i].record()
         bench.step(args.warmup + i)
-        ends[i].record()
+    ev_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kern_avg_s = sum(kern_ms) / K * 1e-3
-    kern_sorted = sorted(kern_ms)
+    kern_avg_s = ev_start.elapsed_time(ev_end) * 1e-3 / K
 
     achieved = bench.bytes / kern_avg_s / 1e9
     traffic = stored_traffic(args.config)
     ceiling = copy_ceiling(torch)
-    log(f"bench: kernel avg {kern_avg_s * 1e6:.2f} us (min {kern_sorted[0] * 1e3:.2f}, "
-        f"median {kern_sorted[K // 2] * 1e3:.2f}), {achieved:.0f} GB/s; "
-        f"copy ceiling {ceiling:.0f} GB/s; wall {wall * 1e3 / K:.2f} ms/step")
+    log(f"bench: kernel avg {kern_avg_s * 1e6:.2f} us, {achieved:.0f} GB/s; "
+        f"copy ceiling {ceiling:.0f} GB/s; wall {wall * 1e3 / K:.3f} ms/step")
+
+    unfused = None
+    if hasattr(bench, "unfused_parts"):
+        parts, unfused_bytes = bench.unfused_parts()
+        us, wall_ms = time_launches(torch, parts, K, args.warmup)
+        total_us = sum(us.values())
+        unfused = {"kernels_us": us, "ms_per_step": wall_ms,
+                   "algorithmic_bytes_per_step": unfused_bytes,
+                   "achieved_GBps": unfused_bytes / (total_us * 1e-6) / 1e9,
+                   "fused_speedup": total_us / (kern_avg_s * 1e6)}
+        log(f"bench: unfused baseline {us} -> fused is {unfused['fused_speedup']:.2f}x faster")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -294,9 +347,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "kernel_avg_us": kern_avg_s * 1e6,
-                     "kernel_median_us": kern_sorted[K // 2] * 1e3,
                      "copy_ceiling_GBps": ceiling},
         "cpu_baseline": cpu,
+        "unfused_baseline": unfused,
     }
     print(json.dumps(rec), flush=True)
 

@@ -97,11 +97,14 @@ enum mf_dtype {
  *                   16-byte aligned.
  *   norm_weight     BF16 [hidden], 16-byte aligned.
  *   output          BF16 [num_tokens, hidden], contiguous, 16-byte aligned.
- *   hidden, top_k   4096 and 8 (the page's fixed specialisation).
+ *   hidden, top_k   256 <= hidden <= 8192 with hidden % 256 == 0 and
+ *                   1 <= top_k <= 32.  The page specialises to 4096 and 8;
+ *                   the library accepts the token-major path's envelope
+ *                   [BEAM] for the index map too.
  *   eps             added to the mean square inside the square root.
  *
  * Errors: NULL pointer (any, when num_tokens > 0) -> MF_ERR_NULL_POINTER;
- * hidden != 4096, top_k != 8, num_tokens < 0 or > INT32_MAX, num_rows < 0,
+ * hidden or top_k outside the envelope, num_tokens < 0 or > INT32_MAX, num_rows < 0,
  * row_stride < hidden -> MF_ERR_BAD_SHAPE; bad weights_dtype
  * -> MF_ERR_BAD_DTYPE; misaligned pointer or row_stride % 8 != 0 ->
  * MF_ERR_MISALIGNED.
@@ -164,6 +167,27 @@ MF_API int beam_moe_finalize(const void *expert_outputs, int64_t capacity,
                       void *output, int64_t live_tokens,
                       const void *post_weight, float routed_scale,
                       float post_eps, int32_t has_norm, void *stream);
+
+/*
+ * mf_rmsnorm - standalone per-token RMSNorm of BF16 rows: the second step of
+ * the unfused strategy (finalize first, normalise separately) that the
+ * [BEAM] fused finalize pages keep for validation and benchmarking, with the
+ * norm of [TPF] (eps inside the root, g = float(norm_weight) + gain_center
+ * in FP32, weight before or after the statistics).  With x = float(input):
+ *   weight_before_norm == 0:  out = x / sqrt(mean(x^2) + eps) * g
+ *   weight_before_norm != 0:  z = x * g;  out = z / sqrt(mean(z^2) + eps)
+ * moe_finalize followed by mf_rmsnorm is the unfused counterpart of
+ * moe_finalize_rmsnorm (it rounds the sum to BF16 in between).
+ *
+ *   input        BF16 [num_tokens, row_stride], row_stride % 8 == 0 and
+ *                >= hidden; only columns [0, hidden) are read.
+ *   norm_weight  BF16 [hidden];  output  BF16 [num_tokens, hidden], contiguous.
+ *   All 16-byte aligned; hidden in the envelope of moe_finalize.
+ * Errors as moe_finalize_rmsnorm.
+ */
+MF_API int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_weight,
+                      void *output, int64_t num_tokens, int32_t hidden, float eps,
+                      float gain_center, int32_t weight_before_norm, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 MF_API const char *mf_status_string(int status);

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   moe_finalize          index-map finalize without a norm
   beam_moe_finalize     token-major finalize with BF16 rounding points and an
                         optional RMSNorm (vLLM "vllm.models.beam.nvidia.moe_finalize")
+  mf_rmsnorm            standalone RMSNorm of BF16 rows (the second step of the
+                        unfused baseline moe_finalize -> mf_rmsnorm)
 """
 from __future__ import annotations
 
@@ -27,8 +29,8 @@ MF_OK = 0
 MF_DTYPE_BF16 = 1
 MF_DTYPE_FP32 = 2
 
-__all__ = ["moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "FinalizeError",
-           "lib", "LIB_PATH"]
+__all__ = ["moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "mf_rmsnorm",
+           "FinalizeError", "lib", "LIB_PATH"]
 
 
 class FinalizeError(ValueError):
@@ -43,14 +45,15 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; build it with "
-            "`python -m moe_expert_output_finalize_amd.build` (or __graft_entry__.build())")
+            "`python moe_expert_output_finalize_amd/build.py` (or __graft_entry__.build())")
     so = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     so.moe_finalize_rmsnorm.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, i64, i32, i32,
                                         f32, f32, i32, vp]
     so.moe_finalize.argtypes = [vp, i64, i64, vp, i32, vp, vp, i64, i32, i32, vp]
     so.beam_moe_finalize.argtypes = [vp, i64, i32, i32, vp, i64, vp, i64, vp, f32, f32, i32, vp]
-    for f in (so.moe_finalize_rmsnorm, so.moe_finalize, so.beam_moe_finalize):
+    so.mf_rmsnorm.argtypes = [vp, i64, vp, vp, i64, i32, f32, f32, i32, vp]
+    for f in (so.moe_finalize_rmsnorm, so.moe_finalize, so.beam_moe_finalize, so.mf_rmsnorm):
         f.restype = i32
     so.mf_status_string.argtypes = [ctypes.c_int]
     so.mf_status_string.restype = ctypes.c_char_p
@@ -183,3 +186,24 @@ def beam_moe_finalize(expert_outputs: torch.Tensor, expert_weights: torch.Tensor
         float(post_eps or 0.0), int(post_eps is not None), _stream(stream, dev))
     _raise_on(name, rc)
     return output
+
+
+def mf_rmsnorm(input: torch.Tensor, norm_weight: torch.Tensor, output: torch.Tensor, *,
+               eps: float, gain_center: float, weight_before_norm: bool, stream=None) -> None:
+    """Standalone per-token RMSNorm of BF16 rows, written into ``output``."""
+    name = "mf_rmsnorm"
+    dev = _check_device(name, input, norm_weight, output)
+    _require(input.dim() == 2 and input.dtype == torch.bfloat16 and
+             (input.stride(1) == 1 or input.shape[1] <= 1), name,
+             "input must be a 2-D bfloat16 tensor with a unit-stride last dimension")
+    _require(output.dim() == 2 and output.dtype == torch.bfloat16 and output.is_contiguous() and
+             output.shape[0] == input.shape[0] and input.shape[1] >= output.shape[1], name,
+             "output must be a contiguous bfloat16 [tokens, hidden] tensor")
+    _require(norm_weight.dim() == 1 and norm_weight.dtype == torch.bfloat16 and
+             norm_weight.is_contiguous() and norm_weight.shape[0] == output.shape[1], name,
+             "norm_weight must be a contiguous bfloat16 [hidden] tensor")
+    stride = input.stride(0) if input.shape[0] > 1 else input.shape[1]
+    rc = lib.mf_rmsnorm(input.data_ptr(), stride, norm_weight.data_ptr(), output.data_ptr(),
+                        output.shape[0], output.shape[1], float(eps), float(gain_center),
+                        int(bool(weight_before_norm)), _stream(stream, dev))
+    _raise_on(name, rc)

@@ -4,11 +4,14 @@
 // no side effect.  The checks are the C form of the parameter contracts on
 // the FlashInfer page "flashinfer.comm.tp_moe_finalize_rmsnorm" (Parameters:
 // shapes, dtypes, unit-stride rows with a row stride that is a multiple of 8
-// elements, 16-byte alignment, hidden 4096 and top-k 8) and of the argument
+// elements, 16-byte alignment) and of the argument
 // checks in beam_moe_finalize on the vLLM page
 // "vllm.models.beam.nvidia.moe_finalize" (1 <= top_k <= 32, hidden a
 // multiple of 256 in [256, 8192], live rows <= capacity, weight rows >= live
 // rows, post_weight only with a norm, nothing to do for zero live rows).
+// The FlashInfer page specialises its finalize+RMSNorm to hidden 4096 and
+// top-k 8; here every entry point accepts the wider envelope of the vLLM
+// checks, 4096 / 8 included.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -24,9 +27,9 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 bool hidden_in_envelope(int32_t hidden) { return hidden >= 256 && hidden <= 8192 && hidden % 256 == 0; }
 
-int launch(const mf::FinalizeArgs &a, mf::Epilogue epi, void *stream)
+int launch(const mf::FinalizeArgs &a, mf::Layout layout, mf::Epilogue epi, void *stream)
 {
-    const hipError_t err = mf::launch_finalize(a, epi, static_cast<hipStream_t>(stream));
+    const hipError_t err = mf::launch_finalize(a, layout, epi, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) {
         snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s (%d)",
                  hipGetErrorString(err), static_cast<int>(err));
@@ -82,7 +85,7 @@ int moe_finalize_rmsnorm(const void *gemm2_permuted, int64_t num_rows, int64_t r
                          void *output, int64_t num_tokens, int32_t hidden, int32_t top_k,
                          float eps, float gain_center, int32_t weight_before_norm, void *stream)
 {
-    if (hidden != 4096 || top_k != 8)
+    if (!hidden_in_envelope(hidden) || top_k < 1 || top_k > 32)
         return MF_ERR_BAD_SHAPE;
     mf::FinalizeArgs a;
     const int rc = check_index_map(gemm2_permuted, num_rows, row_stride, expert_weights,
@@ -99,7 +102,8 @@ int moe_finalize_rmsnorm(const void *gemm2_permuted, int64_t num_rows, int64_t r
     a.gain = static_cast<const uint16_t *>(norm_weight);
     a.eps = eps;
     a.gain_center = gain_center;
-    return launch(a, weight_before_norm ? mf::Epilogue::kRmsNormWeightFirst : mf::Epilogue::kRmsNorm,
+    return launch(a, mf::Layout::kIndexMap,
+                  weight_before_norm ? mf::Epilogue::kRmsNormWeightFirst : mf::Epilogue::kRmsNorm,
                   stream);
 }
 
@@ -118,7 +122,7 @@ int moe_finalize(const void *gemm2_permuted, int64_t num_rows, int64_t row_strid
         return rc;
     if (num_tokens == 0)
         return MF_OK;
-    return launch(a, mf::Epilogue::kRound, stream);
+    return launch(a, mf::Layout::kIndexMap, mf::Epilogue::kRound, stream);
 }
 
 int beam_moe_finalize(const void *expert_outputs, int64_t capacity, int32_t top_k, int32_t hidden,
@@ -154,7 +158,39 @@ int beam_moe_finalize(const void *expert_outputs, int64_t capacity, int32_t top_
     a.top_k = top_k;
     a.eps = post_eps;
     a.routed_scale = routed_scale;
-    return launch(a, has_norm ? mf::Epilogue::kBeamNorm : mf::Epilogue::kBeam, stream);
+    return launch(a, mf::Layout::kTokenMajor,
+                  has_norm ? mf::Epilogue::kBeamNorm : mf::Epilogue::kBeam, stream);
+}
+
+int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_weight, void *output,
+               int64_t num_tokens, int32_t hidden, float eps, float gain_center,
+               int32_t weight_before_norm, void *stream)
+{
+    if (!hidden_in_envelope(hidden) || num_tokens < 0 || num_tokens > INT32_MAX ||
+        row_stride < hidden)
+        return MF_ERR_BAD_SHAPE;
+    if (row_stride % 8 != 0)
+        return MF_ERR_MISALIGNED;
+    if (num_tokens == 0)
+        return MF_OK;
+    if (!input || !norm_weight || !output)
+        return MF_ERR_NULL_POINTER;
+    if (!aligned(input, 16) || !aligned(norm_weight, 16) || !aligned(output, 16))
+        return MF_ERR_MISALIGNED;
+    mf::FinalizeArgs a{};
+    a.rows = static_cast<const uint16_t *>(input);
+    a.row_stride = row_stride;
+    a.num_rows = num_tokens;
+    a.gain = static_cast<const uint16_t *>(norm_weight);
+    a.out = static_cast<uint16_t *>(output);
+    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.hidden = hidden;
+    a.top_k = 1;
+    a.eps = eps;
+    a.gain_center = gain_center;
+    return launch(a, mf::Layout::kDirect,
+                  weight_before_norm ? mf::Epilogue::kRmsNormWeightFirst : mf::Epilogue::kRmsNorm,
+                  stream);
 }
 
 const char *mf_status_string(int status)

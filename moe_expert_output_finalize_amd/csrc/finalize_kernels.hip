@@ -62,7 +62,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;
-constexpr uint32_t kNumXcd = 8;
 
 // ------------------------------------------------------------ BF16 -------
 
@@ -150,7 +149,7 @@ __device__ __forceinline__ float block_sum(float v)
 
 // ------------------------------------------------------------ kernel -----
 
-// LAYOUT_IDX: rows come through the index map (else token major).
+// L: where slot rows come from (index map, token major, or one row per token).
 // KC: top_k when known at compile time (0: read a.top_k).
 // VPT: 16-byte vectors per thread; EXACT: hidden/8 == blockDim.x * VPT.
 // Slots whose rows one workgroup has in flight at once (see finalize_kernel).
@@ -162,7 +161,7 @@ constexpr int slots_in_flight(int kc, int vpt)
 template <int VPT>
 constexpr int max_team() { return VPT == 1 ? 1024 : VPT == 2 ? 512 : 256; }
 
-template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
+template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
 __global__ void __launch_bounds__(max_team<VPT>())
 finalize_kernel(const FinalizeArgs a)
 {
@@ -214,14 +213,19 @@ finalize_kernel(const FinalizeArgs a)
             w[b] = 0.0f;
             row_off[b] = 0;
             if (live) {
-                w[b] = load_weight<W_BF16>(a.weights, tk + k);
-                if constexpr (LAYOUT_IDX) {
+                if constexpr (L == Layout::kIndexMap) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + k);
                     const int32_t i = a.idx[tk + k];
                     ok[b] = i >= 0 && (int64_t)i < a.num_rows;
                     row_off[b] = (int64_t)i * a.row_stride;
-                } else {
+                } else if constexpr (L == Layout::kTokenMajor) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + k);
                     ok[b] = true;
                     row_off[b] = (tk + k) * (int64_t)a.hidden;
+                } else {   // kDirect: fma(1, x, +0) == x exactly
+                    w[b] = 1.0f;
+                    ok[b] = true;
+                    row_off[b] = t * a.row_stride;
                 }
             }
         }
@@ -387,7 +391,7 @@ inline size_t residency_lds(int hidden, int slots)
 #endif
 }
 
-template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI, int KC>
+template <Layout L, bool W_BF16, Epilogue EPI, int KC>
 hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
 {
     const int n = a.hidden / 256;
@@ -397,23 +401,23 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     const size_t lds = residency_lds(a.hidden, slots_in_flight(KC, vpt > 0 ? vpt : 1));
     switch (vpt) {
     case 8:
-        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 8, true>), grid,
+        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid,
                            dim3(nv / 8), lds, s, a);
         break;
     case 4:
-        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 4, true>), grid,
+        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid,
                            dim3(nv / 4), lds, s, a);
         break;
     case 2:
-        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 2, true>), grid,
+        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid,
                            dim3(nv / 2), lds, s, a);
         break;
     case 1:
-        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 1, true>), grid,
+        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid,
                            dim3(nv), lds, s, a);
         break;
     default:   // n odd: 32 (n + 1) threads, the last half wave idle
-        hipLaunchKernelGGL((finalize_kernel<LAYOUT_IDX, W_BF16, EPI, KC, 1, false>), grid,
+        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false>), grid,
                            dim3(nv + 32), lds, s, a);
         break;
     }
@@ -421,41 +425,63 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
 }
 
 // Compile-time slot counts for the common top-k values, runtime otherwise.
-template <bool LAYOUT_IDX, bool W_BF16, Epilogue EPI>
+template <Layout L, bool W_BF16, Epilogue EPI>
 hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
 {
     switch (a.top_k) {
     case 8:
-        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 8>(a, s);
+        return launch_shape<L, W_BF16, EPI, 8>(a, s);
     case 16:
-        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 16>(a, s);
+        return launch_shape<L, W_BF16, EPI, 16>(a, s);
     default:
-        return launch_shape<LAYOUT_IDX, W_BF16, EPI, 0>(a, s);
+        return launch_shape<L, W_BF16, EPI, 0>(a, s);
     }
 }
 
 template <Epilogue EPI>
 hipError_t launch_index_map(const FinalizeArgs &a, hipStream_t s)
 {
-    return a.weights_bf16 ? launch_topk<true, true, EPI>(a, s)
-                          : launch_topk<true, false, EPI>(a, s);
+    return a.weights_bf16 ? launch_topk<Layout::kIndexMap, true, EPI>(a, s)
+                          : launch_topk<Layout::kIndexMap, false, EPI>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_finalize(const FinalizeArgs &a, Epilogue epi, hipStream_t s)
+hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, hipStream_t s)
 {
-    switch (epi) {
-    case Epilogue::kRound:
-        return launch_index_map<Epilogue::kRound>(a, s);
-    case Epilogue::kRmsNorm:
-        return launch_index_map<Epilogue::kRmsNorm>(a, s);
-    case Epilogue::kRmsNormWeightFirst:
-        return launch_index_map<Epilogue::kRmsNormWeightFirst>(a, s);
-    case Epilogue::kBeam:
-        return launch_topk<false, false, Epilogue::kBeam>(a, s);
-    case Epilogue::kBeamNorm:
-        return launch_topk<false, false, Epilogue::kBeamNorm>(a, s);
+    switch (layout) {
+    case Layout::kIndexMap:
+        switch (epi) {
+        case Epilogue::kRound:
+            return launch_index_map<Epilogue::kRound>(a, s);
+        case Epilogue::kRmsNorm:
+            return launch_index_map<Epilogue::kRmsNorm>(a, s);
+        case Epilogue::kRmsNormWeightFirst:
+            return launch_index_map<Epilogue::kRmsNormWeightFirst>(a, s);
+        default:
+            break;
+        }
+        break;
+    case Layout::kTokenMajor:
+        switch (epi) {
+        case Epilogue::kBeam:
+            return launch_topk<Layout::kTokenMajor, false, Epilogue::kBeam>(a, s);
+        case Epilogue::kBeamNorm:
+            return launch_topk<Layout::kTokenMajor, false, Epilogue::kBeamNorm>(a, s);
+        default:
+            break;
+        }
+        break;
+    case Layout::kDirect:
+        switch (epi) {
+        case Epilogue::kRmsNorm:
+            return launch_shape<Layout::kDirect, false, Epilogue::kRmsNorm, 1>(a, s);
+        case Epilogue::kRmsNormWeightFirst:
+            return launch_shape<Layout::kDirect, false, Epilogue::kRmsNormWeightFirst, 1>(a, s);
+        default:
+            break;
+        }
+        break;
     }
     return hipErrorInvalidValue;
 }

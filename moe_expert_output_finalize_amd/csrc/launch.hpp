@@ -8,6 +8,13 @@
 
 namespace mf {
 
+// Where a token's slot rows come from.
+enum class Layout : int {
+    kIndexMap,    // row idx[t, k] of a [num_rows, row_stride] matrix; invalid -> skipped
+    kTokenMajor,  // row (t * K + k) of a [capacity * K, hidden] matrix
+    kDirect,      // one slot, row t of a [T, row_stride] matrix, weight 1
+};
+
 // What the kernel does after the FP32 routed sum.
 enum class Epilogue : int {
     kRound,              // out = bf16(acc)
@@ -19,8 +26,8 @@ enum class Epilogue : int {
 
 // Arguments of one launch; validated by the caller.
 struct FinalizeArgs {
-    const uint16_t *rows;     // BF16 row matrix (index map) or [cap, K, H] (token major)
-    int64_t row_stride;       // elements between rows (index map only)
+    const uint16_t *rows;     // BF16 row matrix (see Layout)
+    int64_t row_stride;       // elements between rows (index map, direct)
     int64_t num_rows;         // valid index range [0, num_rows) (index map only)
     const int32_t *idx;       // [T, K] index map, or nullptr for token major
     const void *weights;      // [T, K] FP32 or BF16
@@ -35,7 +42,10 @@ struct FinalizeArgs {
     float routed_scale;
 };
 
-// Enqueue the finalize on `stream`; returns the launch status.
-hipError_t launch_finalize(const FinalizeArgs &a, Epilogue epi, hipStream_t stream);
+// Enqueue the finalize on `stream`; returns the launch status.  Supported
+// pairs: index map with kRound / kRmsNorm / kRmsNormWeightFirst; token major
+// with kBeam / kBeamNorm; direct with kRmsNorm / kRmsNormWeightFirst.
+hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi,
+                           hipStream_t stream);
 
 }  // namespace mf

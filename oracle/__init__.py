@@ -56,7 +56,8 @@ def _load():
                                                     i64, i32, i32, f32, f32, i32]
         lib.oracle_beam_moe_finalize.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp,
                                                  f32, f32, i32]
-        for name in ("oracle_routed_sum", "oracle_moe_finalize",
+        lib.oracle_rmsnorm.argtypes = [vp, i64, vp, vp, i64, i32, f32, f32, i32]
+        for name in ("oracle_routed_sum", "oracle_moe_finalize", "oracle_rmsnorm",
                      "oracle_moe_finalize_rmsnorm", "oracle_beam_moe_finalize"):
             getattr(lib, name).restype = i32
         _lib = lib
@@ -150,6 +151,20 @@ def moe_finalize_rmsnorm(gemm2_permuted, expert_weights, expanded_idx_to_permute
         _ptr(g), rows, stride, _ptr(w), is32, _ptr(idx), _ptr(nw), _ptr(out), T,
         hidden, K, float(eps), float(gain_center), int(bool(weight_before_norm))),
         "moe_finalize_rmsnorm")
+    return out
+
+
+def rmsnorm(x, norm_weight, *, eps: float, gain_center: float,
+            weight_before_norm: bool) -> np.ndarray:
+    """BF16 bits [T, hidden] of the standalone RMSNorm of BF16 rows ``x``
+    (uint16 [T, >= hidden], unit stride in the last dimension)."""
+    nw = np.ascontiguousarray(norm_weight, dtype=np.uint16)
+    hidden = nw.shape[0]
+    g, T, stride = _rows_view(x, hidden)
+    out = np.empty((T, hidden), dtype=np.uint16)
+    _check(_load().oracle_rmsnorm(_ptr(g), stride, _ptr(nw), _ptr(out), T, hidden, float(eps),
+                                  float(gain_center), int(bool(weight_before_norm))),
+           "rmsnorm")
     return out
 
 

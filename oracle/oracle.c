@@ -14,6 +14,10 @@
  *   [RMOE] FlashInfer API page
  *          "flashinfer.fused_moe.trtllm_fp8_per_tensor_scale_routed_moe":
  *          Returns section (the unfinalized triple when do_finalize is off).
+ *   The unfused strategy of beam_moe_finalize_norm_residual_norm on [BEAM]
+ *   (finalize first, normalise in a separate step, kept for validation and
+ *   benchmarking) motivates oracle_rmsnorm: the [TPF] norm applied to rows
+ *   that were already rounded to BF16.
  *
  * Precision policy.  Where the pages fix a precision it is kept exactly:
  *   - the routed reduction is FP32 (weights of either dtype become FP32 and
@@ -240,6 +244,44 @@ int oracle_moe_finalize_rmsnorm(const uint16_t *gemm2_permuted, int64_t num_rows
         }
     }
     free(acc); free(g); free(z);
+    return 0;
+}
+
+/*
+ * Standalone RMSNorm of BF16 rows (the second step of the unfused strategy):
+ * the [TPF] norm with x = f32(input) in place of the FP32 routed sum.
+ *   input   BF16 rows, row t starts at input + t*row_stride (elements)
+ */
+int oracle_rmsnorm(const uint16_t *input, int64_t row_stride,
+                   const uint16_t *norm_weight, uint16_t *output,
+                   int64_t num_tokens, int32_t hidden, float eps,
+                   float gain_center, int32_t weight_before_norm)
+{
+    if (hidden <= 0 || num_tokens < 0 || row_stride < hidden)
+        return -1;
+    float *g = (float *)malloc(sizeof(float) * (size_t)hidden);
+    double *z = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!g || !z) {
+        free(g); free(z);
+        return -2;
+    }
+    for (int32_t h = 0; h < hidden; ++h)
+        g[h] = oracle_bf16_to_f32(norm_weight[h]) + gain_center;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const uint16_t *x = input + t * row_stride;
+        for (int32_t h = 0; h < hidden; ++h) {
+            double v = (double)oracle_bf16_to_f32(x[h]);
+            z[h] = weight_before_norm ? v * (double)g[h] : v;
+        }
+        double inv = inv_rms(z, hidden, (double)eps);
+        for (int32_t h = 0; h < hidden; ++h) {
+            double y = z[h] * inv;
+            if (!weight_before_norm)
+                y *= (double)g[h];
+            output[t * hidden + h] = oracle_round_to_bf16(y);
+        }
+    }
+    free(g); free(z);
     return 0;
 }
 

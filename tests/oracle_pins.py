@@ -560,9 +560,40 @@ def pin_beam_layout(orc):
     assert_bits_equal(a, b, "token-major layout")
 
 
+def pin_standalone_rmsnorm(orc):
+    """The standalone norm of BF16 rows equals torch's float64 rms_norm
+    (within 1 ulp, almost always exact); on rows whose routed sum is exactly
+    the row (one valid slot, weight 1) it equals the fused finalize+norm bit
+    for bit; and finalize-then-norm stays within 1 ulp of the fused path."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    H, T = 2048, 24
+    x = wl.normal_bf16(rng, (T, H + 64))
+    nw = wl.normal_bf16(rng, (H,), std=0.1)
+    for wbn, gc in ((False, 1.0), (True, 0.0), (False, -0.25)):
+        got = orc.rmsnorm(x, nw, eps=1e-6, gain_center=gc, weight_before_norm=wbn)
+        xa = wl.bf16_bits_to_f32(x[:, :H])
+        assert_within_ulp(got, _norm_expect(xa, nw, gc, 1e-6, wbn), 1, 0.995,
+                          f"standalone wbn={wbn}")
+        idx = np.full((T, 8), -1, np.int32)
+        idx[:, 5] = np.arange(T)
+        w = np.zeros((T, 8), np.float32)
+        w[:, 5] = 1.0
+        fused = orc.moe_finalize_rmsnorm(x, w, idx, nw, eps=1e-6, gain_center=gc,
+                                         weight_before_norm=wbn)
+        assert_bits_equal(got, fused, "norm of exact rows == fused")
+    case = wl.tiny(num_tokens=32, num_rows=256)
+    fin = orc.moe_finalize(case.gemm2, case.expert_weights, case.idx, case.hidden)
+    unf = orc.rmsnorm(fin, case.norm_weight, eps=case.eps, gain_center=case.gain_center,
+                      weight_before_norm=case.weight_before_norm)
+    fus = orc.moe_finalize_rmsnorm(case.gemm2, case.expert_weights, case.idx, case.norm_weight,
+                                   eps=case.eps, gain_center=case.gain_center,
+                                   weight_before_norm=case.weight_before_norm)
+    assert_within_ulp(unf, fus, 2, 0.5, "unfused vs fused")
+
+
 ALL_PINS = [pin_bf16_widening, pin_rne_against_torch, pin_rne_binary64_single_rounding,
             pin_routed_sum_exact, pin_routed_sum_error_bound, pin_masking_invariants,
             pin_identity_copy, pin_bf16_weights, pin_finalize_rounds_sum,
             pin_rmsnorm_library, pin_rmsnorm_special_case, pin_rmsnorm_closed_forms,
             pin_rmsnorm_invariants, pin_beam_worked_example,
-            pin_beam_against_torch_pipeline, pin_beam_layout]
+            pin_beam_against_torch_pipeline, pin_beam_layout, pin_standalone_rmsnorm]

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "mf_status_string",
-            "mf_last_error_message"} <= names
+    assert {"moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "mf_rmsnorm",
+            "mf_status_string", "mf_last_error_message"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -78,7 +78,9 @@ def beam(**over):
 @pytest.mark.parametrize("over,want", [
     (dict(T=0), OK),
     (dict(T=0, g=None, w=None, idx=None, nw=None, out=None), OK),
-    (dict(H=2048), SHAPE), (dict(K=4), SHAPE), (dict(T=-1), SHAPE), (dict(rows=-1), SHAPE),
+    (dict(T=0, H=2048, K=4), OK), (dict(T=0, H=256, K=1), OK), (dict(T=0, H=8192, K=32, stride=8192), OK),
+    (dict(H=2000), SHAPE), (dict(H=8448, stride=8448), SHAPE), (dict(K=0), SHAPE), (dict(K=33), SHAPE),
+    (dict(T=-1), SHAPE), (dict(rows=-1), SHAPE),
     (dict(T=1 << 31), SHAPE), (dict(stride=4088), SHAPE),
     (dict(stride=4100), ALIGN), (dict(wdt=0), DTYPE), (dict(wdt=3), DTYPE),
     (dict(g=None), NULLP), (dict(w=None), NULLP), (dict(idx=None), NULLP),
@@ -114,6 +116,24 @@ def test_finalize_validation(over, want):
 ])
 def test_beam_validation(over, want):
     assert beam(**over) == want
+
+
+def norm(**over):
+    a = dict(x=P, stride=4096, nw=P, out=P, T=16, H=4096, eps=1e-6, gc=1.0, wbn=0, stream=None)
+    a.update(over)
+    return mf.lib.mf_rmsnorm(a["x"], a["stride"], a["nw"], a["out"], a["T"], a["H"], a["eps"],
+                             a["gc"], a["wbn"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=0), OK), (dict(T=0, x=None, nw=None, out=None), OK), (dict(T=0, H=256), OK),
+    (dict(H=200), SHAPE), (dict(H=8448, stride=8448), SHAPE), (dict(T=-1), SHAPE),
+    (dict(stride=4000), SHAPE), (dict(stride=4100), ALIGN),
+    (dict(x=None), NULLP), (dict(nw=None), NULLP), (dict(out=None), NULLP),
+    (dict(x=P + 2), ALIGN), (dict(nw=P + 8), ALIGN), (dict(out=P + 4), ALIGN),
+])
+def test_standalone_norm_validation(over, want):
+    assert norm(**over) == want
 
 
 def test_binding_rejects_host_tensors():

@@ -161,6 +161,22 @@ def test_finalize_envelope(hidden):
 
 
 @pytest.mark.parametrize("hidden", SWEEP_H)
+def test_rmsnorm_envelope(hidden):
+    """Index-map finalize + RMSNorm over the whole hidden / top-k envelope."""
+    for K in SWEEP_K:
+        for wdt, wbn, gc in (("fp32", False, 1.0), ("bf16", True, 0.0), ("fp32", True, -0.5)):
+            T = 11
+            c = wl.make_index_map_case(3000 + hidden + K, num_tokens=T, hidden=hidden, top_k=K,
+                                       num_rows=T * K + 5, row_stride=hidden + 8 * (K % 3),
+                                       weights_dtype=wdt, invalid_frac=0.15, poison=True,
+                                       nan_rows_beyond=2, weight_before_norm=wbn,
+                                       gain_center=gc)
+            d = IndexMapOnDevice(c)
+            assert_within_ulp(gpu_rmsnorm(d), oracle_rmsnorm(c), 1, NORM_MIN_EXACT,
+                              f"H={hidden} K={K} {wdt} wbn={wbn}")
+
+
+@pytest.mark.parametrize("hidden", SWEEP_H)
 def test_beam_envelope(hidden):
     for K in SWEEP_K:
         for norm, pw, scale in ((False, None, 1.75), (True, 0.05, 1.0), (True, None, 0.3)):
@@ -175,6 +191,49 @@ def test_beam_envelope(hidden):
                 assert_within_ulp(got, want, 1, NORM_MIN_EXACT, what)
             else:
                 assert_bits_equal(got, want, what)
+
+
+# ----------------------------------------------- unfused baseline (f2) ------
+
+def gpu_unfused(d: IndexMapOnDevice, **kw):
+    """moe_finalize into a BF16 intermediate, then mf_rmsnorm."""
+    c = d.case
+    args = dict(eps=c.eps, gain_center=c.gain_center, weight_before_norm=c.weight_before_norm)
+    args.update(kw)
+    mid = d.new_output()
+    mf.moe_finalize(d.gemm2, d.weights, d.idx, mid)
+    out = d.new_output()
+    mf.mf_rmsnorm(mid, d.norm_weight, out, **args)
+    sync()
+    return host_bits(mid), host_bits(out)
+
+
+@pytest.mark.parametrize("name", list(INDEX_CONFIGS))
+def test_unfused_pipeline_config(name):
+    c = case(name, INDEX_CONFIGS[name])
+    d = IndexMapOnDevice(c)
+    mid, out = gpu_unfused(d)
+    want_mid = oracle_finalize(c)
+    assert_bits_equal(mid, want_mid, f"{name} unfused intermediate")
+    want = oracle.rmsnorm(want_mid, c.norm_weight, eps=c.eps, gain_center=c.gain_center,
+                          weight_before_norm=c.weight_before_norm)
+    assert_within_ulp(out, want, 1, NORM_MIN_EXACT, f"{name} unfused norm")
+
+
+@pytest.mark.parametrize("hidden", SWEEP_H)
+def test_standalone_norm_envelope(hidden):
+    rng = np.random.Generator(np.random.PCG64(4000 + hidden))
+    T = 13
+    x = wl.normal_bf16(rng, (T, hidden + 64))
+    x[:, hidden:] = 0x7FC0                       # padding never read
+    nw = wl.normal_bf16(rng, (hidden,), mean=1.0, std=0.1)
+    xd, nwd = dev_bf16(x), dev_bf16(nw)
+    for wbn, gc in ((False, 0.0), (True, 1.0), (False, -0.5)):
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda")
+        mf.mf_rmsnorm(xd[:, :hidden], nwd, out, eps=1e-5, gain_center=gc, weight_before_norm=wbn)
+        sync()
+        want = oracle.rmsnorm(x, nw, eps=1e-5, gain_center=gc, weight_before_norm=wbn)
+        assert_within_ulp(host_bits(out), want, 1, NORM_MIN_EXACT, f"H={hidden} wbn={wbn}")
 
 
 # ------------------------------------------------------------ edge cases ----

@@ -54,6 +54,10 @@ MUTANTS = {
     "weight_row_stride": ("(const float *)weights + t * top_k", "(const float *)weights + t"),
     "row_stride_ignored": ("rows + i * row_stride", "rows + i * (int64_t)hidden"),
     "output_sign": ("double y = z[h] * inv;", "double y = -z[h] * inv;"),
+    "standalone_row_stride": ("const uint16_t *x = input + t * row_stride;",
+                              "const uint16_t *x = input + t * (int64_t)hidden;"),
+    "standalone_weight_first_ignored": ("z[h] = weight_before_norm ? v * (double)g[h] : v;",
+                                        "z[h] = v;"),
 }
 
 _RUNNER = r"""
