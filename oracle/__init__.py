@@ -57,8 +57,14 @@ def _load():
         lib.oracle_beam_moe_finalize.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp,
                                                  f32, f32, i32]
         lib.oracle_rmsnorm.argtypes = [vp, i64, vp, vp, i64, i32, f32, f32, i32]
+        lib.oracle_beam_norm_residual_norm.argtypes = [vp, i64, vp, vp, vp, vp, vp, i64, i32,
+                                                       f32, f32, f32, f32, i32, i32]
+        lib.oracle_beam_moe_finalize_norm_residual_norm.argtypes = [
+            vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, i32]
         for name in ("oracle_routed_sum", "oracle_moe_finalize", "oracle_rmsnorm",
-                     "oracle_moe_finalize_rmsnorm", "oracle_beam_moe_finalize"):
+                     "oracle_moe_finalize_rmsnorm", "oracle_beam_moe_finalize",
+                     "oracle_beam_norm_residual_norm",
+                     "oracle_beam_moe_finalize_norm_residual_norm"):
             getattr(lib, name).restype = i32
         _lib = lib
     return _lib
@@ -188,3 +194,52 @@ def beam_moe_finalize(expert_outputs, expert_weights, live_tokens: int,
         float(routed_scale), float(post_eps or 0.0), int(post_eps is not None)),
         "beam_moe_finalize")
     return out
+
+
+# --------------------------------------- residual add + next norm (f1) -------
+# The consumer these two follow is not defined on the pages; see oracle.c for
+# the reading (PARITY UNPINNED against the pages).
+
+def beam_norm_residual_norm(x, residual, post_weight=None, post_eps=None, next_weight=None,
+                            next_eps=None, scales=None):
+    """(hidden, normalized or None) BF16 bits of post-norm -> residual add ->
+    next norm on BF16 rows ``x`` (uint16 [T, >= H]) and ``residual`` ([T, H])."""
+    r = np.ascontiguousarray(residual, dtype=np.uint16)
+    T, H = r.shape
+    g, T2, stride = _rows_view(x, H)
+    assert T2 == T
+    pw = None if post_weight is None else np.ascontiguousarray(post_weight, dtype=np.uint16)
+    nw = None if next_weight is None else np.ascontiguousarray(next_weight, dtype=np.uint16)
+    hid = np.empty((T, H), dtype=np.uint16)
+    nrm = np.empty((T, H), dtype=np.uint16) if next_eps is not None else None
+    sx, sr = scales if scales is not None else (1.0, 1.0)
+    _check(_load().oracle_beam_norm_residual_norm(
+        _ptr(g), stride, _ptr(r), _ptr(pw), _ptr(nw), _ptr(hid), _ptr(nrm), T, H,
+        float(post_eps or 0.0), float(next_eps or 0.0), float(sx), float(sr),
+        int(post_eps is not None), int(next_eps is not None)), "beam_norm_residual_norm")
+    return hid, nrm
+
+
+def beam_moe_finalize_norm_residual_norm(expert_outputs, expert_weights, residual,
+                                         post_weight=None, post_eps=None, next_weight=None,
+                                         next_eps=None, scales=None, routed_scale=1.0):
+    """(hidden, normalized or None) BF16 bits of the token-major finalize
+    followed by the residual add and next norm, for residual.shape[0] tokens."""
+    e = expert_outputs
+    assert e.dtype == np.uint16 and e.ndim == 3 and e.flags.c_contiguous
+    capacity, K, H = e.shape
+    r = np.ascontiguousarray(residual, dtype=np.uint16)
+    T = r.shape[0]
+    w = np.ascontiguousarray(expert_weights, dtype=np.float32)
+    assert w.shape[1] == K and w.shape[0] >= T and r.shape == (T, H)
+    pw = None if post_weight is None else np.ascontiguousarray(post_weight, dtype=np.uint16)
+    nw = None if next_weight is None else np.ascontiguousarray(next_weight, dtype=np.uint16)
+    hid = np.empty((T, H), dtype=np.uint16)
+    nrm = np.empty((T, H), dtype=np.uint16) if next_eps is not None else None
+    sx, sr = scales if scales is not None else (1.0, 1.0)
+    _check(_load().oracle_beam_moe_finalize_norm_residual_norm(
+        _ptr(e), capacity, K, H, _ptr(w), _ptr(r), _ptr(pw), _ptr(nw), _ptr(hid), _ptr(nrm), T,
+        float(routed_scale), float(post_eps or 0.0), float(next_eps or 0.0), float(sx),
+        float(sr), int(post_eps is not None), int(next_eps is not None)),
+        "beam_moe_finalize_norm_residual_norm")
+    return hid, nrm

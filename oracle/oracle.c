@@ -14,6 +14,12 @@
  *   [RMOE] FlashInfer API page
  *          "flashinfer.fused_moe.trtllm_fp8_per_tensor_scale_routed_moe":
  *          Returns section (the unfinalized triple when do_finalize is off).
+ *   [BEAM] also: beam_moe_finalize_norm_residual_norm (docstring and wrapper)
+ *          and, through its unfused strategy, the consumer it calls after
+ *          beam_moe_finalize, beam_norm_residual_norm, whose body is not on
+ *          the page.  oracle_beam_norm_residual_norm below is the plainest
+ *          reading of that consumer (see there); PARITY UNPINNED against
+ *          the pages for the two scales and the rounding point of hidden.
  *   The unfused strategy of beam_moe_finalize_norm_residual_norm on [BEAM]
  *   (finalize first, normalise in a separate step, kept for validation and
  *   benchmarking) motivates oracle_rmsnorm: the [TPF] norm applied to rows
@@ -333,4 +339,103 @@ int oracle_beam_moe_finalize(const uint16_t *expert_outputs, int64_t capacity,
     }
     free(acc); free(s); free(sb);
     return 0;
+}
+
+/*
+ * Post-norm, residual add and next norm of BF16 rows x: the consumer that
+ * the unfused strategy of [BEAM] beam_moe_finalize_norm_residual_norm calls
+ * after beam_moe_finalize.  Its definition is not on the pages; the reading
+ * taken here (PARITY UNPINNED against the pages):
+ *   y      = has_post ? bf16(x / sqrt(mean(x^2) + post_eps) * pw) : x
+ *            (pw = post_weight, or 1 when NULL; the norm of beam_moe_finalize)
+ *   hidden = bf16(scale_x * y + scale_res * residual)
+ *            (the wrapper passes the scales pair, or (1, 1) when it is None,
+ *            so they are read as multipliers of the two summands)
+ *   normalized = bf16(hidden / sqrt(mean(hidden^2) + next_eps) * nw)
+ *            (nw = next_weight or 1; computed from hidden as stored in BF16,
+ *            only when has_next)
+ *   x, residual  BF16 rows; row t of x at x + t*row_stride, of residual at
+ *                residual + t*hidden.
+ */
+int oracle_beam_norm_residual_norm(const uint16_t *x, int64_t row_stride,
+                                   const uint16_t *residual,
+                                   const uint16_t *post_weight,
+                                   const uint16_t *next_weight,
+                                   uint16_t *hidden_out, uint16_t *normalized_out,
+                                   int64_t num_tokens, int32_t hidden,
+                                   float post_eps, float next_eps,
+                                   float scale_x, float scale_res,
+                                   int32_t has_post, int32_t has_next)
+{
+    if (hidden <= 0 || num_tokens < 0 || row_stride < hidden)
+        return -1;
+    double *v = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!v)
+        return -2;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const uint16_t *xr = x + t * row_stride;
+        const uint16_t *rr = residual + t * (int64_t)hidden;
+        uint16_t *hr = hidden_out + t * (int64_t)hidden;
+        for (int32_t h = 0; h < hidden; ++h)
+            v[h] = (double)oracle_bf16_to_f32(xr[h]);
+        if (has_post) {
+            double inv = inv_rms(v, hidden, (double)post_eps);
+            for (int32_t h = 0; h < hidden; ++h) {
+                double y = v[h] * inv;
+                if (post_weight)
+                    y *= (double)oracle_bf16_to_f32(post_weight[h]);
+                v[h] = (double)oracle_bf16_to_f32(oracle_round_to_bf16(y));
+            }
+        }
+        for (int32_t h = 0; h < hidden; ++h) {
+            double sum = (double)scale_x * v[h] +
+                         (double)scale_res * (double)oracle_bf16_to_f32(rr[h]);
+            hr[h] = oracle_round_to_bf16(sum);
+            v[h] = (double)oracle_bf16_to_f32(hr[h]);
+        }
+        if (!has_next)
+            continue;
+        double inv = inv_rms(v, hidden, (double)next_eps);
+        uint16_t *nr = normalized_out + t * (int64_t)hidden;
+        for (int32_t h = 0; h < hidden; ++h) {
+            double y = v[h] * inv;
+            if (next_weight)
+                y *= (double)oracle_bf16_to_f32(next_weight[h]);
+            nr[h] = oracle_round_to_bf16(y);
+        }
+    }
+    free(v);
+    return 0;
+}
+
+/*
+ * [BEAM] beam_moe_finalize_norm_residual_norm: beam_moe_finalize of the
+ * first num_tokens tokens (with its optional post-norm) followed by
+ * oracle_beam_norm_residual_norm without a second post-norm, exactly the
+ * page's unfused strategy.  weight rows >= num_tokens, capacity >= num_tokens.
+ */
+int oracle_beam_moe_finalize_norm_residual_norm(
+    const uint16_t *expert_outputs, int64_t capacity, int32_t top_k,
+    int32_t hidden, const float *expert_weights, const uint16_t *residual,
+    const uint16_t *post_weight, const uint16_t *next_weight,
+    uint16_t *hidden_out, uint16_t *normalized_out, int64_t num_tokens,
+    float routed_scale, float post_eps, float next_eps, float scale_x,
+    float scale_res, int32_t has_post, int32_t has_next)
+{
+    if (num_tokens < 0 || num_tokens > capacity)
+        return -1;
+    uint16_t *fin = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(num_tokens > 0 ? num_tokens : 1) *
+                                       (size_t)hidden);
+    if (!fin)
+        return -2;
+    int rc = oracle_beam_moe_finalize(expert_outputs, capacity, top_k, hidden,
+                                      expert_weights, fin, num_tokens, post_weight,
+                                      routed_scale, post_eps, has_post);
+    if (rc == 0)
+        rc = oracle_beam_norm_residual_norm(fin, hidden, residual, NULL, next_weight,
+                                            hidden_out, normalized_out, num_tokens,
+                                            hidden, 0.0f, next_eps, scale_x, scale_res,
+                                            0, has_next);
+    free(fin);
+    return rc;
 }

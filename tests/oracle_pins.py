@@ -591,9 +591,73 @@ def pin_standalone_rmsnorm(orc):
     assert_within_ulp(unf, fus, 2, 0.5, "unfused vs fused")
 
 
+def _torch_bf16_add(a_bits, b_bits):
+    """torch's BF16 + BF16 (computed in FP32, rounded once to BF16)."""
+    a = torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).view(torch.bfloat16)
+    b = torch.from_numpy(np.ascontiguousarray(b_bits).view(np.int16)).view(torch.bfloat16)
+    return (a + b).view(torch.int16).numpy().view(np.uint16)
+
+
+def _rmsnorm_expect(bits, weight_bits, eps):
+    v = torch.from_numpy(wl.bf16_bits_to_f32(bits).astype(np.float64))
+    w = None if weight_bits is None else torch.from_numpy(
+        wl.bf16_bits_to_f32(weight_bits).astype(np.float64))
+    y = torch.nn.functional.rms_norm(v, (v.shape[-1],), weight=w, eps=eps)
+    return table_round_to_bf16(y.numpy()).reshape(bits.shape)
+
+
+def pin_residual_next_norm(orc):
+    """Residual add and next norm (the reading of the off-page consumer):
+    zero residual is the identity, the add is torch's BF16 add, the next norm
+    is torch's float64 rms_norm of hidden as stored in BF16, the post-norm is
+    the beam post-norm, scales[0] multiplies x and scales[1] the residual,
+    and the fused op is beam_moe_finalize followed by the consumer."""
+    rng = np.random.Generator(np.random.PCG64(51))
+    T, H = 12, 1024
+    x = wl.normal_bf16(rng, (T, H + 64))
+    x[:, H:] = 0x7FC0
+    res = wl.normal_bf16(rng, (T, H))
+    pw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.05)
+    nw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.1)
+    zero = np.zeros((T, H), np.uint16)
+    hid, nrm = orc.beam_norm_residual_norm(x, zero)
+    assert nrm is None
+    assert_bits_equal(hid, x[:, :H], "zero residual")
+    hid, nrm = orc.beam_norm_residual_norm(x, res, next_weight=nw, next_eps=1e-6)
+    assert_within_ulp(hid, _torch_bf16_add(x[:, :H], res), 1, 0.999, "residual add")
+    assert_within_ulp(nrm, _rmsnorm_expect(hid, nw, 1e-6), 1, 0.99, "next norm")
+    hid, nrm = orc.beam_norm_residual_norm(x, res, next_eps=1e-5)
+    assert_within_ulp(nrm, _rmsnorm_expect(hid, None, 1e-5), 1, 0.99, "next norm, no weight")
+    hid, _ = orc.beam_norm_residual_norm(x, zero, post_weight=pw, post_eps=1e-6)
+    post = _rmsnorm_expect(x[:, :H], pw, 1e-6)
+    assert_within_ulp(hid, post, 1, 0.99, "post norm")
+    # the post-normed value is rounded to BF16 before the residual add
+    hid, _ = orc.beam_norm_residual_norm(x, res, post_weight=pw, post_eps=1e-6)
+    assert_within_ulp(hid, _torch_bf16_add(post, res), 1, 0.99, "post norm, then add")
+    hid, _ = orc.beam_norm_residual_norm(x, res, scales=(2.0, 0.0))
+    assert_bits_equal(hid, table_round_to_bf16(2.0 * wl.bf16_bits_to_f32(x[:, :H])).reshape(T, H),
+                      "scales[0] scales x")
+    hid, _ = orc.beam_norm_residual_norm(x, res, scales=(0.0, 1.0))
+    assert_bits_equal(hid, res, "scales[1] scales the residual")
+    # fused == finalize then consumer
+    case = wl.make_token_major_case(52, capacity=14, top_k=4, hidden=H, live_tokens=T,
+                                    routed_scale=1.5, post_eps=1e-6, post_weight_std=0.05,
+                                    poison_dead=True)
+    fin = orc.beam_moe_finalize(case.expert_outputs, case.expert_weights, T, 1.5,
+                                case.post_weight, 1e-6)
+    want_h, want_n = orc.beam_norm_residual_norm(fin, res, next_weight=nw, next_eps=1e-6,
+                                                 scales=(0.5, 2.0))
+    got_h, got_n = orc.beam_moe_finalize_norm_residual_norm(
+        case.expert_outputs, case.expert_weights, res, case.post_weight, 1e-6, nw, 1e-6,
+        (0.5, 2.0), 1.5)
+    assert_bits_equal(got_h, want_h, "fused hidden")
+    assert_bits_equal(got_n, want_n, "fused normalized")
+
+
 ALL_PINS = [pin_bf16_widening, pin_rne_against_torch, pin_rne_binary64_single_rounding,
             pin_routed_sum_exact, pin_routed_sum_error_bound, pin_masking_invariants,
             pin_identity_copy, pin_bf16_weights, pin_finalize_rounds_sum,
             pin_rmsnorm_library, pin_rmsnorm_special_case, pin_rmsnorm_closed_forms,
             pin_rmsnorm_invariants, pin_beam_worked_example,
-            pin_beam_against_torch_pipeline, pin_beam_layout, pin_standalone_rmsnorm]
+            pin_beam_against_torch_pipeline, pin_beam_layout, pin_standalone_rmsnorm,
+            pin_residual_next_norm]

@@ -56,6 +56,16 @@ MUTANTS = {
     "output_sign": ("double y = z[h] * inv;", "double y = -z[h] * inv;"),
     "standalone_row_stride": ("const uint16_t *x = input + t * row_stride;",
                               "const uint16_t *x = input + t * (int64_t)hidden;"),
+    "residual_dropped": ("(double)scale_x * v[h] +\n                         (double)scale_res * (double)oracle_bf16_to_f32(rr[h]);",
+                         "(double)scale_x * v[h];"),
+    "scales_swapped": ("(double)scale_x * v[h] +\n                         (double)scale_res *",
+                       "(double)scale_res * v[h] +\n                         (double)scale_x *"),
+    "next_norm_from_unrounded_hidden": ("v[h] = (double)oracle_bf16_to_f32(hr[h]);", "v[h] = sum;"),
+    "next_weight_ignored": ("if (next_weight)\n                y *= (double)oracle_bf16_to_f32(next_weight[h]);",
+                            "(void)next_weight;"),
+    "residual_row_stride": ("rr = residual + t * (int64_t)hidden;", "rr = residual + t * row_stride;"),
+    "consumer_post_norm_unrounded": ("v[h] = (double)oracle_bf16_to_f32(oracle_round_to_bf16(y));",
+                                     "v[h] = y;"),
     "standalone_weight_first_ignored": ("z[h] = weight_before_norm ? v * (double)g[h] : v;",
                                         "z[h] = v;"),
 }
