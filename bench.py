@@ -46,6 +46,8 @@ WORKLOADS = {
     "tiny": "tiny finalize+RMSNorm: 16 tokens, hidden 4096, top-k 8, 5% invalid slots",
     "beam4": "token-major finalize, no norm: 3000 live of 4096, top-k 8, hidden 7168, scale 2.5",
     "beam5": "token-major finalize + post RMSNorm: 16000 live of 16384, top-k 16, hidden 2048",
+    "beam5_residual": "token-major finalize + post RMSNorm + residual add + next RMSNorm: "
+                      "16000 of 16384 tokens, top-k 16, hidden 2048",
 }
 
 
@@ -207,6 +209,61 @@ def time_launches(torch, fns, steps: int, warmup: int):
     return us, wall_ms
 
 
+class ResidualBench(TokenMajorBench):
+    """beam_moe_finalize_norm_residual_norm on the beam5 shape: post-norm,
+    residual add and next norm fused into the finalize."""
+
+    def __init__(self, c, torch, mf):
+        import numpy as np
+        import workloads as wl
+        super().__init__(c, torch, mf)
+        rng = np.random.Generator(np.random.PCG64(5))
+        L, H = c.live_tokens, c.hidden
+        dev = torch.device("cuda:0")
+        res = wl.normal_bf16(rng, (L, H))
+        nw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.1)
+        self.res_host, self.nw_host = res, nw
+        self.res = torch.from_numpy(res.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.nw = torch.from_numpy(nw.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.outs2 = [torch.empty_like(o) for o in self.outs]
+        self.next_eps = 1e-6
+        # gather + residual + hidden + normalized + weights + both norm weights
+        self.bytes = (L * c.top_k * H * 2 + L * H * 2 * 3 + L * c.top_k * 4 + 2 * H * 2)
+
+    def step(self, i: int):
+        s = i % self.sets
+        c = self.c
+        self.mf.beam_moe_finalize_norm_residual_norm(
+            self.rows[s], self.w, self.res, self.pw, c.post_eps, self.nw, self.next_eps, None,
+            c.routed_scale, hidden_out=self.outs[s], normalized_out=self.outs2[s])
+
+    # The page's unfused strategy: beam_moe_finalize, then the consumer.
+    def unfused_parts(self):
+        c, torch = self.c, self.torch
+        mids = [torch.empty_like(o) for o in self.outs]
+
+        def finalize(i):
+            s = i % self.sets
+            self.mf.beam_moe_finalize(self.rows[s], self.w, mids[s], c.routed_scale, self.pw,
+                                      c.post_eps)
+
+        def consumer(i):
+            s = i % self.sets
+            self.mf.beam_norm_residual_norm(mids[s], self.res, None, None, self.nw,
+                                            self.next_eps, None, hidden_out=self.outs[s],
+                                            normalized_out=self.outs2[s])
+        extra = 2 * c.live_tokens * c.hidden * 2
+        return [("beam_moe_finalize", finalize), ("beam_norm_residual_norm", consumer)], \
+            self.bytes + extra
+
+    def cpu_oracle(self, oracle, tokens: slice):
+        c = self.c
+        n = len(range(*tokens.indices(c.live_tokens)))
+        oracle.beam_moe_finalize_norm_residual_norm(
+            c.expert_outputs[tokens], c.expert_weights[tokens], self.res_host[tokens],
+            c.post_weight, c.post_eps, self.nw_host, self.next_eps, None, c.routed_scale)
+
+
 def cpu_baseline(bench, seconds: float) -> dict:
     """The oracle (single-threaded C) on whole passes over the workload's
     tokens, repeated until `seconds` of CPU time have been spent."""
@@ -276,8 +333,13 @@ def main():
     import workloads as wl
 
     log(f"bench: generating the {args.config} workload")
-    c = wl.CONFIGS[args.config]()
-    bench = (IndexMapBench if isinstance(c, wl.IndexMapCase) else TokenMajorBench)(c, torch, mf)
+    if args.config == "beam5_residual":
+        c = wl.beam5()
+        bench = ResidualBench(c, torch, mf)
+    else:
+        c = wl.CONFIGS[args.config]()
+        bench = (IndexMapBench if isinstance(c, wl.IndexMapCase) else TokenMajorBench)(
+            c, torch, mf)
     log(f"bench: {bench.sets} rotating buffer sets, {bench.bytes} algorithmic bytes/step")
 
     for i in range(args.warmup):

@@ -189,6 +189,57 @@ MF_API int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_we
                       void *output, int64_t num_tokens, int32_t hidden, float eps,
                       float gain_center, int32_t weight_before_norm, void *stream);
 
+/*
+ * beam_moe_finalize_norm_residual_norm - token-major finalize fused with the
+ * residual add and the next layer's norm [BEAM
+ * beam_moe_finalize_norm_residual_norm].  The page defines the operation as
+ * equal to its unfused strategy: beam_moe_finalize (with its optional
+ * post-norm) followed by a residual/next-norm consumer whose body is not on
+ * the page.  This library reads that consumer as (PARITY UNPINNED against the
+ * pages for the scales and the rounding point of hidden):
+ *   y          = beam_moe_finalize output of token t (BF16)
+ *   hidden     = bf16(scale_x * y + scale_res * residual[t])
+ *   normalized = bf16(hidden / sqrt(mean(hidden^2) + next_eps) * nw)
+ * where nw = next_weight (or 1 when NULL) and normalized is computed from
+ * hidden as stored.  The page passes its `scales` pair as (scale_x,
+ * scale_res), or (1, 1) when the pair is absent.
+ *
+ *   expert_outputs, expert_weights, capacity, top_k, hidden, routed_scale,
+ *   post_weight, post_eps, has_post_norm   as beam_moe_finalize
+ *   residual        BF16 [num_tokens, hidden], contiguous, 16-byte aligned
+ *   next_weight     BF16 [hidden] or NULL (only with has_next_norm)
+ *   hidden_out      BF16 [num_tokens, hidden], contiguous
+ *   normalized_out  BF16 [num_tokens, hidden], required iff has_next_norm
+ *   num_tokens      tokens to finalize: <= capacity and <= weight_rows
+ * Errors as beam_moe_finalize; a norm weight without its norm ->
+ * MF_ERR_BAD_ARGUMENT.
+ */
+MF_API int beam_moe_finalize_norm_residual_norm(
+    const void *expert_outputs, int64_t capacity, int32_t top_k, int32_t hidden,
+    const float *expert_weights, int64_t weight_rows, const void *residual,
+    const void *post_weight, const void *next_weight, void *hidden_out,
+    void *normalized_out, int64_t num_tokens, float routed_scale, float post_eps,
+    float next_eps, float scale_x, float scale_res, int32_t has_post_norm,
+    int32_t has_next_norm, void *stream);
+
+/*
+ * beam_norm_residual_norm - the consumer of the unfused strategy on its own
+ * (second step of the [BEAM] unfused baseline): optional post-norm of the
+ * BF16 rows x (as in beam_moe_finalize, rounded to BF16), then hidden and
+ * normalized as in beam_moe_finalize_norm_residual_norm.  Same reading,
+ * PARITY UNPINNED against the pages.
+ *
+ *   x         BF16 [num_tokens, row_stride], row_stride % 8 == 0, >= hidden
+ *   other arguments as beam_moe_finalize_norm_residual_norm.
+ */
+MF_API int beam_norm_residual_norm(const void *x, int64_t row_stride, const void *residual,
+                                   const void *post_weight, const void *next_weight,
+                                   void *hidden_out, void *normalized_out,
+                                   int64_t num_tokens, int32_t hidden, float post_eps,
+                                   float next_eps, float scale_x, float scale_res,
+                                   int32_t has_post_norm, int32_t has_next_norm,
+                                   void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MF_API const char *mf_status_string(int status);
 

@@ -14,6 +14,12 @@ Entry points (same names as the C ABI):
                         optional RMSNorm (vLLM "vllm.models.beam.nvidia.moe_finalize")
   mf_rmsnorm            standalone RMSNorm of BF16 rows (the second step of the
                         unfused baseline moe_finalize -> mf_rmsnorm)
+  beam_moe_finalize_norm_residual_norm
+                        token-major finalize fused with the residual add and the
+                        next norm (vLLM page, same function name)
+  beam_norm_residual_norm
+                        the residual add and next norm on their own (second step
+                        of the page's unfused strategy)
 """
 from __future__ import annotations
 
@@ -30,6 +36,7 @@ MF_DTYPE_BF16 = 1
 MF_DTYPE_FP32 = 2
 
 __all__ = ["moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "mf_rmsnorm",
+           "beam_moe_finalize_norm_residual_norm", "beam_norm_residual_norm",
            "FinalizeError", "lib", "LIB_PATH"]
 
 
@@ -53,7 +60,12 @@ def _load() -> ctypes.CDLL:
     so.moe_finalize.argtypes = [vp, i64, i64, vp, i32, vp, vp, i64, i32, i32, vp]
     so.beam_moe_finalize.argtypes = [vp, i64, i32, i32, vp, i64, vp, i64, vp, f32, f32, i32, vp]
     so.mf_rmsnorm.argtypes = [vp, i64, vp, vp, i64, i32, f32, f32, i32, vp]
-    for f in (so.moe_finalize_rmsnorm, so.moe_finalize, so.beam_moe_finalize, so.mf_rmsnorm):
+    so.beam_moe_finalize_norm_residual_norm.argtypes = [
+        vp, i64, i32, i32, vp, i64, vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, i32, vp]
+    so.beam_norm_residual_norm.argtypes = [vp, i64, vp, vp, vp, vp, vp, i64, i32, f32, f32, f32,
+                                           f32, i32, i32, vp]
+    for f in (so.moe_finalize_rmsnorm, so.moe_finalize, so.beam_moe_finalize, so.mf_rmsnorm,
+              so.beam_moe_finalize_norm_residual_norm, so.beam_norm_residual_norm):
         f.restype = i32
     so.mf_status_string.argtypes = [ctypes.c_int]
     so.mf_status_string.restype = ctypes.c_char_p
@@ -207,3 +219,101 @@ def mf_rmsnorm(input: torch.Tensor, norm_weight: torch.Tensor, output: torch.Ten
                         output.shape[0], output.shape[1], float(eps), float(gain_center),
                         int(bool(weight_before_norm)), _stream(stream, dev))
     _raise_on(name, rc)
+
+
+def _opt_ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _outputs(name, residual, next_eps, hidden_out, normalized_out):
+    """(hidden, normalized) destinations: the given tensors, or new ones."""
+    def ok(t):
+        return (t.shape == residual.shape and t.dtype == torch.bfloat16 and t.is_contiguous()
+                and t.device == residual.device)
+    if hidden_out is None:
+        hidden_out = torch.empty_like(residual)
+    _require(ok(hidden_out), name, "hidden_out must be a contiguous bfloat16 tensor like residual")
+    if next_eps is None:
+        return hidden_out, None
+    if normalized_out is None:
+        normalized_out = torch.empty_like(residual)
+    _require(ok(normalized_out), name,
+             "normalized_out must be a contiguous bfloat16 tensor like residual")
+    return hidden_out, normalized_out
+
+
+def _check_norm_weight(name, w, eps, hidden, what):
+    if w is None:
+        return
+    _require(eps is not None, name, f"{what} needs its eps")
+    _require(w.shape == (hidden,) and w.dtype == torch.bfloat16 and w.is_contiguous(), name,
+             f"{what} must be a contiguous bfloat16 [hidden] tensor")
+
+
+def beam_moe_finalize_norm_residual_norm(
+        expert_outputs: torch.Tensor, expert_weights: torch.Tensor, residual: torch.Tensor,
+        post_weight: torch.Tensor | None, post_eps: float | None,
+        next_weight: torch.Tensor | None, next_eps: float | None,
+        scales: tuple[float, float] | None, routed_scale: float = 1.0, stream=None, *,
+        hidden_out: torch.Tensor | None = None, normalized_out: torch.Tensor | None = None):
+    """Fused token-major finalize -> (post-norm) -> residual add -> next norm
+    for residual.shape[0] tokens; returns (hidden, normalized or None).
+
+    ``expert_outputs`` is [capacity, top_k, hidden] (the producer's
+    [capacity * top_k, hidden] rows viewed per token).  ``hidden_out`` and
+    ``normalized_out`` may be given to write into existing tensors."""
+    name = "beam_moe_finalize_norm_residual_norm"
+    dev = _check_device(name, expert_outputs, expert_weights, residual, post_weight,
+                        next_weight)
+    _require(expert_outputs.dim() == 3 and expert_weights.dim() == 2 and residual.dim() == 2,
+             name, "expected [capacity, top_k, hidden], [rows, top_k] and [tokens, hidden]")
+    capacity, top_k, hidden = expert_outputs.shape
+    _require(expert_outputs.dtype == torch.bfloat16 and residual.dtype == torch.bfloat16,
+             name, "expert_outputs and residual must be bfloat16")
+    _require(expert_weights.dtype == torch.float32, name, "expert_weights must be float32")
+    for t in (expert_outputs, expert_weights, residual):
+        _require(t.is_contiguous(), name, "tensors must be contiguous")
+    _require(residual.shape[1] == hidden and expert_weights.shape[1] == top_k, name,
+             "hidden / top_k mismatch")
+    _check_norm_weight(name, post_weight, post_eps, hidden, "post_weight")
+    _check_norm_weight(name, next_weight, next_eps, hidden, "next_weight")
+    out_h, out_n = _outputs(name, residual, next_eps, hidden_out, normalized_out)
+    sx, sr = scales if scales is not None else (1.0, 1.0)
+    rc = lib.beam_moe_finalize_norm_residual_norm(
+        expert_outputs.data_ptr(), capacity, top_k, hidden, expert_weights.data_ptr(),
+        expert_weights.shape[0], residual.data_ptr(), _opt_ptr(post_weight),
+        _opt_ptr(next_weight), out_h.data_ptr(), _opt_ptr(out_n), residual.shape[0],
+        float(routed_scale), float(post_eps or 0.0), float(next_eps or 0.0), float(sx),
+        float(sr), int(post_eps is not None), int(next_eps is not None), _stream(stream, dev))
+    _raise_on(name, rc)
+    return out_h, out_n
+
+
+def beam_norm_residual_norm(x: torch.Tensor, residual: torch.Tensor,
+                            post_weight: torch.Tensor | None, post_eps: float | None,
+                            next_weight: torch.Tensor | None, next_eps: float | None,
+                            scales: tuple[float, float] | None, stream=None, *,
+                            hidden_out: torch.Tensor | None = None,
+                            normalized_out: torch.Tensor | None = None):
+    """(Post-norm) -> residual add -> next norm of BF16 rows ``x``; returns
+    (hidden, normalized or None), optionally written into given tensors."""
+    name = "beam_norm_residual_norm"
+    dev = _check_device(name, x, residual, post_weight, next_weight)
+    _require(x.dim() == 2 and residual.dim() == 2 and x.dtype == torch.bfloat16 and
+             residual.dtype == torch.bfloat16, name, "x and residual must be 2-D bfloat16")
+    _require(x.stride(1) == 1 or x.shape[1] <= 1, name, "x needs a unit-stride last dimension")
+    _require(residual.is_contiguous() and x.shape[0] == residual.shape[0] and
+             x.shape[1] >= residual.shape[1], name, "x / residual shape mismatch")
+    hidden = residual.shape[1]
+    _check_norm_weight(name, post_weight, post_eps, hidden, "post_weight")
+    _check_norm_weight(name, next_weight, next_eps, hidden, "next_weight")
+    out_h, out_n = _outputs(name, residual, next_eps, hidden_out, normalized_out)
+    sx, sr = scales if scales is not None else (1.0, 1.0)
+    stride = x.stride(0) if x.shape[0] > 1 else x.shape[1]
+    rc = lib.beam_norm_residual_norm(
+        x.data_ptr(), stride, residual.data_ptr(), _opt_ptr(post_weight), _opt_ptr(next_weight),
+        out_h.data_ptr(), _opt_ptr(out_n), residual.shape[0], hidden, float(post_eps or 0.0),
+        float(next_eps or 0.0), float(sx), float(sr), int(post_eps is not None),
+        int(next_eps is not None), _stream(stream, dev))
+    _raise_on(name, rc)
+    return out_h, out_n

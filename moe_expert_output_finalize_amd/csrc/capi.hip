@@ -193,6 +193,94 @@ int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_weight, v
                   stream);
 }
 
+int beam_moe_finalize_norm_residual_norm(
+    const void *expert_outputs, int64_t capacity, int32_t top_k, int32_t hidden,
+    const float *expert_weights, int64_t weight_rows, const void *residual,
+    const void *post_weight, const void *next_weight, void *hidden_out, void *normalized_out,
+    int64_t num_tokens, float routed_scale, float post_eps, float next_eps, float scale_x,
+    float scale_res, int32_t has_post_norm, int32_t has_next_norm, void *stream)
+{
+    if (top_k < 1 || top_k > 32 || !hidden_in_envelope(hidden))
+        return MF_ERR_BAD_SHAPE;
+    if (capacity < 0 || num_tokens < 0 || num_tokens > capacity || num_tokens > INT32_MAX ||
+        weight_rows < num_tokens)
+        return MF_ERR_BAD_SHAPE;
+    if ((post_weight && !has_post_norm) || (next_weight && !has_next_norm))
+        return MF_ERR_BAD_ARGUMENT;
+    if (num_tokens == 0)
+        return MF_OK;
+    if (!expert_outputs || !expert_weights || !residual || !hidden_out ||
+        (has_next_norm && !normalized_out))
+        return MF_ERR_NULL_POINTER;
+    if (!aligned(expert_outputs, 16) || !aligned(expert_weights, 4) || !aligned(residual, 16) ||
+        !aligned(post_weight, 16) || !aligned(next_weight, 16) || !aligned(hidden_out, 16) ||
+        !aligned(normalized_out, 16))
+        return MF_ERR_MISALIGNED;
+    mf::FinalizeArgs a{};
+    a.rows = static_cast<const uint16_t *>(expert_outputs);
+    a.row_stride = hidden;
+    a.num_rows = capacity * top_k;
+    a.weights = expert_weights;
+    a.gain = static_cast<const uint16_t *>(post_weight);
+    a.out = static_cast<uint16_t *>(hidden_out);
+    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.hidden = hidden;
+    a.top_k = top_k;
+    a.eps = post_eps;
+    a.routed_scale = routed_scale;
+    a.residual = static_cast<const uint16_t *>(residual);
+    a.gain2 = static_cast<const uint16_t *>(next_weight);
+    a.out2 = static_cast<uint16_t *>(normalized_out);
+    a.eps2 = next_eps;
+    a.scale_x = scale_x;
+    a.scale_res = scale_res;
+    a.has_post = has_post_norm != 0;
+    a.has_next = has_next_norm != 0;
+    return launch(a, mf::Layout::kTokenMajor, mf::Epilogue::kResidualNorm, stream);
+}
+
+int beam_norm_residual_norm(const void *x, int64_t row_stride, const void *residual,
+                            const void *post_weight, const void *next_weight, void *hidden_out,
+                            void *normalized_out, int64_t num_tokens, int32_t hidden,
+                            float post_eps, float next_eps, float scale_x, float scale_res,
+                            int32_t has_post_norm, int32_t has_next_norm, void *stream)
+{
+    if (!hidden_in_envelope(hidden) || num_tokens < 0 || num_tokens > INT32_MAX ||
+        row_stride < hidden)
+        return MF_ERR_BAD_SHAPE;
+    if (row_stride % 8 != 0)
+        return MF_ERR_MISALIGNED;
+    if ((post_weight && !has_post_norm) || (next_weight && !has_next_norm))
+        return MF_ERR_BAD_ARGUMENT;
+    if (num_tokens == 0)
+        return MF_OK;
+    if (!x || !residual || !hidden_out || (has_next_norm && !normalized_out))
+        return MF_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(post_weight, 16) ||
+        !aligned(next_weight, 16) || !aligned(hidden_out, 16) || !aligned(normalized_out, 16))
+        return MF_ERR_MISALIGNED;
+    mf::FinalizeArgs a{};
+    a.rows = static_cast<const uint16_t *>(x);
+    a.row_stride = row_stride;
+    a.num_rows = num_tokens;
+    a.gain = static_cast<const uint16_t *>(post_weight);
+    a.out = static_cast<uint16_t *>(hidden_out);
+    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.hidden = hidden;
+    a.top_k = 1;
+    a.eps = post_eps;
+    a.routed_scale = 1.0f;   // bf16(bf16(x) * 1) == x: the rounding points are exact here
+    a.residual = static_cast<const uint16_t *>(residual);
+    a.gain2 = static_cast<const uint16_t *>(next_weight);
+    a.out2 = static_cast<uint16_t *>(normalized_out);
+    a.eps2 = next_eps;
+    a.scale_x = scale_x;
+    a.scale_res = scale_res;
+    a.has_post = has_post_norm != 0;
+    a.has_next = has_next_norm != 0;
+    return launch(a, mf::Layout::kDirect, mf::Epilogue::kResidualNorm, stream);
+}
+
 const char *mf_status_string(int status)
 {
     switch (status) {
@@ -201,7 +289,7 @@ const char *mf_status_string(int status)
     case MF_ERR_BAD_SHAPE: return "a size is negative, inconsistent or outside the supported envelope";
     case MF_ERR_BAD_DTYPE: return "unsupported weights dtype";
     case MF_ERR_MISALIGNED: return "a pointer or row stride is not 16-byte aligned";
-    case MF_ERR_BAD_ARGUMENT: return "inconsistent optional arguments (post_weight without a norm)";
+    case MF_ERR_BAD_ARGUMENT: return "inconsistent optional arguments (a norm weight without its norm)";
     case MF_ERR_LAUNCH_FAILED: return "the HIP kernel launch failed";
     default: return "unknown status";
     }

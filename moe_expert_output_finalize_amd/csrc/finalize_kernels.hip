@@ -123,7 +123,9 @@ __device__ __forceinline__ float dpp_mov(float v)
 
 // Sum of v over the workgroup, returned to every thread.  All threads of the
 // workgroup must call it (it contains a barrier when there are several waves).
-__device__ __forceinline__ float block_sum(float v)
+// Two sums in one kernel use different banks, so the second's LDS writes
+// cannot overtake a slower wave's reads of the first.
+__device__ __forceinline__ float block_sum(float v, int bank = 0)
 {
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
@@ -137,13 +139,13 @@ __device__ __forceinline__ float block_sum(float v)
     const int waves = blockDim.x / kWave;
     if (waves == 1)
         return s;
-    __shared__ float part[kMaxWaves];
+    __shared__ float part[2][kMaxWaves];
     if ((threadIdx.x & (kWave - 1)) == 0)
-        part[threadIdx.x / kWave] = s;
+        part[bank][threadIdx.x / kWave] = s;
     __syncthreads();
     s = 0.0f;
     for (int i = 0; i < waves; ++i)
-        s += part[i];
+        s += part[bank][i];
     return s;
 }
 
@@ -171,6 +173,8 @@ finalize_kernel(const FinalizeArgs a)
     static_assert(KB >= 1 && (KC == 0 || KC % KB == 0), "slot batch must divide top_k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
+    constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
+                                   EPI == Epilogue::kResidualNorm;
     const int top_k = KC > 0 ? KC : a.top_k;
     const int team = blockDim.x;
     const int lane = threadIdx.x;
@@ -181,14 +185,28 @@ finalize_kernel(const FinalizeArgs a)
     // The norm weight is shared by every token and stays cache resident;
     // fetch it first so its latency hides under the gather.
     u32x4 gv[VPT];
-    if constexpr (kNorm) {
-        const bool have = EPI != Epilogue::kBeamNorm || a.gain != nullptr;
+    if constexpr (kNorm || EPI == Epilogue::kResidualNorm) {
+        const bool have = (EPI != Epilogue::kBeamNorm && EPI != Epilogue::kResidualNorm) ||
+                          a.gain != nullptr;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int j = lane + i * team;
             gv[i] = (u32x4){0u, 0u, 0u, 0u};
             if (have && (EXACT || j < nv))
                 gv[i] = reinterpret_cast<const u32x4 *>(a.gain)[j];
+        }
+    }
+
+    // The residual row of this token, for the residual epilogue.
+    u32x4 rv[VPT];
+    if constexpr (EPI == Epilogue::kResidualNorm) {
+        const u32x4 *rr = reinterpret_cast<const u32x4 *>(a.residual + t * (int64_t)a.hidden);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int j = lane + i * team;
+            rv[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (EXACT || j < nv)
+                rv[i] = load_row_vec(rr + j);
         }
     }
 
@@ -275,7 +293,7 @@ finalize_kernel(const FinalizeArgs a)
         return;
     }
 
-    if constexpr (EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm) {
+    if constexpr (kBeamRounding) {
         // r = bf16(acc); s = bf16(r * routed_scale); s is kept widened in acc.
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -294,6 +312,87 @@ finalize_kernel(const FinalizeArgs a)
         }
         if constexpr (EPI == Epilogue::kBeam)
             return;
+    }
+
+    if constexpr (EPI == Epilogue::kResidualNorm) {
+        // Optional post-norm of s, rounded to BF16.
+        if (a.has_post) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
+            ss = block_sum(ss, 0);
+            const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float y0 = acc[i][2 * q] * inv, y1 = acc[i][2 * q + 1] * inv;
+                    if (a.gain) {
+                        y0 *= elem(gv[i], 2 * q);
+                        y1 *= elem(gv[i], 2 * q + 1);
+                    }
+                    const uint32_t p = pack_bf16x2(y0, y1);
+                    acc[i][2 * q] = bf16_lo(p);
+                    acc[i][2 * q + 1] = bf16_hi(p);
+                }
+        }
+        // hidden = bf16(scale_x * y + scale_res * residual), kept widened in acc.
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float h0 = __builtin_fmaf(a.scale_x, acc[i][2 * q],
+                                                a.scale_res * elem(rv[i], 2 * q));
+                const float h1 = __builtin_fmaf(a.scale_x, acc[i][2 * q + 1],
+                                                a.scale_res * elem(rv[i], 2 * q + 1));
+                const uint32_t p = pack_bf16x2(h0, h1);
+                o[q] = p;
+                acc[i][2 * q] = bf16_lo(p);
+                acc[i][2 * q + 1] = bf16_hi(p);
+            }
+            store(i, o);
+        }
+        if (!a.has_next)
+            return;
+        // normalized = bf16(hidden * inv_rms(hidden) * next_weight)
+        u32x4 nv2[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int j = lane + i * team;
+            nv2[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (a.gain2 && (EXACT || j < nv))
+                nv2[i] = reinterpret_cast<const u32x4 *>(a.gain2)[j];
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
+        ss = block_sum(ss, 1);
+        const float inv = rsqrtf(ss / (float)a.hidden + a.eps2);
+        uint16_t *out2_row = a.out2 + t * (int64_t)a.hidden;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float y0 = acc[i][2 * q] * inv, y1 = acc[i][2 * q + 1] * inv;
+                if (a.gain2) {
+                    y0 *= elem(nv2[i], 2 * q);
+                    y1 *= elem(nv2[i], 2 * q + 1);
+                }
+                o[q] = pack_bf16x2(y0, y1);
+            }
+            const int j = lane + i * team;
+            if (EXACT || j < nv)
+                store_out_vec(reinterpret_cast<u32x4 *>(out2_row) + j, o);
+        }
+        return;
     }
 
     if constexpr (kNorm) {
@@ -468,6 +567,8 @@ hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, h
             return launch_topk<Layout::kTokenMajor, false, Epilogue::kBeam>(a, s);
         case Epilogue::kBeamNorm:
             return launch_topk<Layout::kTokenMajor, false, Epilogue::kBeamNorm>(a, s);
+        case Epilogue::kResidualNorm:
+            return launch_topk<Layout::kTokenMajor, false, Epilogue::kResidualNorm>(a, s);
         default:
             break;
         }
@@ -478,6 +579,8 @@ hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, h
             return launch_shape<Layout::kDirect, false, Epilogue::kRmsNorm, 1>(a, s);
         case Epilogue::kRmsNormWeightFirst:
             return launch_shape<Layout::kDirect, false, Epilogue::kRmsNormWeightFirst, 1>(a, s);
+        case Epilogue::kResidualNorm:
+            return launch_shape<Layout::kDirect, false, Epilogue::kResidualNorm, 1>(a, s);
         default:
             break;
         }

@@ -22,6 +22,9 @@ enum class Epilogue : int {
     kRmsNormWeightFirst, // z = acc * g; out = bf16(z * inv_rms(z))
     kBeam,               // out = bf16(bf16(acc) * routed_scale)
     kBeamNorm,           // s = as kBeam; out = bf16(s * inv_rms(s) * post_weight)
+    kResidualNorm,       // s = as kBeam; y = has_post ? bf16(s * inv_rms(s) * post_weight) : s;
+                         // out = h = bf16(scale_x * y + scale_res * residual);
+                         // out2 = bf16(h * inv_rms(h) * next_weight) when has_next
 };
 
 // Arguments of one launch; validated by the caller.
@@ -40,11 +43,19 @@ struct FinalizeArgs {
     float eps;
     float gain_center;
     float routed_scale;
+    // kResidualNorm only
+    const uint16_t *residual; // BF16 [T, H]
+    const uint16_t *gain2;    // BF16 [H] next_weight (nullable)
+    uint16_t *out2;           // BF16 [T, H] normalized (when has_next)
+    float eps2;               // next_eps
+    float scale_x, scale_res;
+    bool has_post, has_next;
 };
 
 // Enqueue the finalize on `stream`; returns the launch status.  Supported
 // pairs: index map with kRound / kRmsNorm / kRmsNormWeightFirst; token major
-// with kBeam / kBeamNorm; direct with kRmsNorm / kRmsNormWeightFirst.
+// with kBeam / kBeamNorm / kResidualNorm; direct with kRmsNorm /
+// kRmsNormWeightFirst / kResidualNorm (routed_scale 1).
 hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi,
                            hipStream_t stream);
 

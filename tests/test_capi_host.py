@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     assert {"moe_finalize_rmsnorm", "moe_finalize", "beam_moe_finalize", "mf_rmsnorm",
+            "beam_moe_finalize_norm_residual_norm", "beam_norm_residual_norm",
             "mf_status_string", "mf_last_error_message"} <= names
 
 
@@ -134,6 +135,48 @@ def norm(**over):
 ])
 def test_standalone_norm_validation(over, want):
     assert norm(**over) == want
+
+
+def fused_rn(**over):
+    a = dict(e=P, cap=16384, K=16, H=2048, w=P, wrows=16384, res=P, pw=P, nw=P, hid=P, nrm=P,
+             T=16000, scale=1.0, peps=1e-6, neps=1e-6, sx=1.0, sr=1.0, hp=1, hn=1, stream=None)
+    a.update(over)
+    return mf.lib.beam_moe_finalize_norm_residual_norm(
+        a["e"], a["cap"], a["K"], a["H"], a["w"], a["wrows"], a["res"], a["pw"], a["nw"], a["hid"],
+        a["nrm"], a["T"], a["scale"], a["peps"], a["neps"], a["sx"], a["sr"], a["hp"], a["hn"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=0), OK), (dict(T=0, e=None, w=None, res=None, hid=None, nrm=None), OK),
+    (dict(K=0), SHAPE), (dict(K=33), SHAPE), (dict(H=2100), SHAPE), (dict(T=16385), SHAPE),
+    (dict(wrows=15999), SHAPE), (dict(cap=-1), SHAPE), (dict(T=-1), SHAPE),
+    (dict(hp=0), ARG), (dict(hn=0), ARG),
+    (dict(e=None), NULLP), (dict(w=None), NULLP), (dict(res=None), NULLP), (dict(hid=None), NULLP),
+    (dict(nrm=None), NULLP), (dict(res=P + 2), ALIGN), (dict(nw=P + 2), ALIGN),
+    (dict(hid=P + 8), ALIGN), (dict(nrm=P + 4), ALIGN), (dict(e=P + 2), ALIGN),
+])
+def test_fused_residual_norm_validation(over, want):
+    assert fused_rn(**over) == want
+
+
+def consumer(**over):
+    a = dict(x=P, stride=2048, res=P, pw=None, nw=P, hid=P, nrm=P, T=100, H=2048, peps=0.0,
+             neps=1e-6, sx=1.0, sr=1.0, hp=0, hn=1, stream=None)
+    a.update(over)
+    return mf.lib.beam_norm_residual_norm(
+        a["x"], a["stride"], a["res"], a["pw"], a["nw"], a["hid"], a["nrm"], a["T"], a["H"],
+        a["peps"], a["neps"], a["sx"], a["sr"], a["hp"], a["hn"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(T=0), OK), (dict(T=0, hn=0, nw=None, nrm=None, x=None, res=None, hid=None), OK),
+    (dict(H=100), SHAPE), (dict(stride=1024), SHAPE), (dict(stride=2052), ALIGN),
+    (dict(pw=P), ARG), (dict(hn=0), ARG), (dict(x=None), NULLP), (dict(res=None), NULLP),
+    (dict(hid=None), NULLP), (dict(nrm=None), NULLP), (dict(x=P + 2), ALIGN),
+])
+def test_consumer_validation(over, want):
+    assert consumer(**over) == want
 
 
 def test_binding_rejects_host_tensors():

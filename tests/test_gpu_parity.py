@@ -236,6 +236,118 @@ def test_standalone_norm_envelope(hidden):
         assert_within_ulp(host_bits(out), want, 1, NORM_MIN_EXACT, f"H={hidden} wbn={wbn}")
 
 
+# ------------------------------- finalize -> residual -> next norm (f1) -----
+
+def residual_case(seed, capacity, top_k, hidden, tokens, post, post_w, nxt, next_w, scales,
+                  routed_scale=1.0):
+    c = wl.make_token_major_case(seed, capacity=capacity, top_k=top_k, hidden=hidden,
+                                 live_tokens=tokens, routed_scale=routed_scale,
+                                 post_eps=1e-6 if post else None,
+                                 post_weight_std=0.05 if (post and post_w) else None,
+                                 poison_dead=True)
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    res = wl.normal_bf16(rng, (tokens, hidden))
+    nw = wl.normal_bf16(rng, (hidden,), mean=1.0, std=0.1) if (nxt and next_w) else None
+    return c, res, nw, (1e-6 if nxt else None), scales
+
+
+def check_residual(c, res, nw, next_eps, scales, what):
+    """Fused op on the GPU vs the oracle.  With a post-norm the finalized
+    value y is only within 1 ulp of the oracle's, and the residual add can
+    amplify that by cancellation, so the comparison is split: the GPU's y
+    against the oracle's finalize, the GPU's hidden / normalized against the
+    oracle's consumer applied to the GPU's own y, and the fused kernel against
+    the two-step GPU path bit for bit.  Without a post-norm y is exact and the
+    fused result is also compared with the oracle's fused op directly."""
+    d = TokenMajorOnDevice(c)
+    T = res.shape[0]
+    resd = dev_bf16(res)
+    nwd = None if nw is None else dev_bf16(nw)
+    h, n = mf.beam_moe_finalize_norm_residual_norm(d.expert_outputs, d.weights, resd,
+                                                   d.post_weight, c.post_eps, nwd, next_eps,
+                                                   scales, c.routed_scale)
+    fin = d.new_output(T)
+    mf.beam_moe_finalize(d.expert_outputs, d.weights, fin, c.routed_scale, d.post_weight,
+                         c.post_eps)
+    h2, n2 = mf.beam_norm_residual_norm(fin, resd, None, None, nwd, next_eps, scales)
+    sync()
+    y = host_bits(fin)
+    want_y = oracle_beam(c, T)
+    if c.post_eps is None:
+        assert_bits_equal(y, want_y, f"{what} y")
+    else:
+        assert_within_ulp(y, want_y, 1, NORM_MIN_EXACT, f"{what} y")
+    got_h, got_n = host_bits(h), (None if n is None else host_bits(n))
+    assert (got_n is None) == (next_eps is None)
+    ch, cn = oracle.beam_norm_residual_norm(y, res, None, None, nw, next_eps, scales)
+    assert_within_ulp(got_h, ch, 1, 0.999, f"{what} hidden")
+    if cn is not None:
+        assert_within_ulp(got_n, cn, 1, NORM_MIN_EXACT, f"{what} normalized")
+    if c.post_eps is None:
+        fh, fn = oracle.beam_moe_finalize_norm_residual_norm(
+            c.expert_outputs, c.expert_weights, res, c.post_weight, c.post_eps, nw, next_eps,
+            scales, c.routed_scale)
+        assert_within_ulp(got_h, fh, 1, 0.999, f"{what} hidden vs fused oracle")
+        if fn is not None:
+            assert_within_ulp(got_n, fn, 1, NORM_MIN_EXACT, f"{what} normalized vs fused oracle")
+    assert_bits_equal(got_h, host_bits(h2), f"{what} fused vs unfused hidden")
+    if got_n is not None:
+        assert_bits_equal(got_n, host_bits(n2), f"{what} fused vs unfused normalized")
+
+
+def test_residual_norm_beam5_shape():
+    """The beam5 shape (capacity 16384, top-k 16, hidden 2048) with a post-norm,
+    the residual add and the next norm over 16000 tokens."""
+    args = residual_case(61, 16384, 16, 2048, 16000, True, True, True, True, None)
+    check_residual(*args, "beam5 post-norm")
+
+
+@pytest.mark.parametrize("post,post_w,nxt,next_w,scales", [
+    (False, False, False, False, None), (False, False, True, True, None),
+    (True, False, True, False, None), (True, True, False, False, (0.5, 2.0)),
+    (False, False, True, True, (1.5, -0.75)), (True, True, True, True, (1.0, 1.0)),
+])
+def test_residual_norm_options(post, post_w, nxt, next_w, scales):
+    for hidden, K, scale in ((7168, 8, 2.5), (2048, 16, 1.0), (768, 3, 0.75), (8192, 1, 1.0)):
+        args = residual_case(70 + hidden + K, 40, K, hidden, 33, post, post_w, nxt, next_w,
+                             scales, scale)
+        check_residual(*args, f"H={hidden} K={K} post={post} next={nxt} scales={scales}")
+
+
+def test_consumer_alone_matches_oracle():
+    """The consumer on its own.  Without a post-norm it is compared with the
+    oracle directly.  With one, the post-normed y (within 1 ulp) is read back
+    through a zero residual, the oracle checks y and the consumer applied to
+    the GPU's y, and the one-call result must equal the two-call one."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    T, H = 50, 4096
+    x = wl.normal_bf16(rng, (T, H + 128))
+    x[:, H:] = 0x7FC0
+    res = wl.normal_bf16(rng, (T, H))
+    pw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.05)
+    nw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.1)
+    xd, resd, pwd, nwd = dev_bf16(x)[:, :H], dev_bf16(res), dev_bf16(pw), dev_bf16(nw)
+    # no post-norm
+    h, n = mf.beam_norm_residual_norm(xd, resd, None, None, nwd, 1e-5, None)
+    sync()
+    wh, wn = oracle.beam_norm_residual_norm(x, res, None, None, nw, 1e-5, None)
+    assert_within_ulp(host_bits(h), wh, 1, 0.999, "consumer hidden")
+    assert_within_ulp(host_bits(n), wn, 1, NORM_MIN_EXACT, "consumer normalized")
+    # with a post-norm
+    zero = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    y, _ = mf.beam_norm_residual_norm(xd, zero, pwd, 1e-6, None, None, None)
+    h1, n1 = mf.beam_norm_residual_norm(xd, resd, pwd, 1e-6, nwd, 1e-5, (0.25, 1.0))
+    h2, n2 = mf.beam_norm_residual_norm(y, resd, None, None, nwd, 1e-5, (0.25, 1.0))
+    sync()
+    wy, _ = oracle.beam_norm_residual_norm(x, np.zeros((T, H), np.uint16), pw, 1e-6)
+    assert_within_ulp(host_bits(y), wy, 1, NORM_MIN_EXACT, "consumer post-norm")
+    assert_bits_equal(host_bits(h1), host_bits(h2), "one call vs two calls, hidden")
+    assert_bits_equal(host_bits(n1), host_bits(n2), "one call vs two calls, normalized")
+    ch, cn = oracle.beam_norm_residual_norm(host_bits(y), res, None, None, nw, 1e-5, (0.25, 1.0))
+    assert_within_ulp(host_bits(h1), ch, 1, 0.999, "consumer hidden after post-norm")
+    assert_within_ulp(host_bits(n1), cn, 1, NORM_MIN_EXACT, "consumer normalized after post-norm")
+
+
 # ------------------------------------------------------------ edge cases ----
 
 @pytest.mark.parametrize("T", [1, 7, 8, 9, 13, 257])
