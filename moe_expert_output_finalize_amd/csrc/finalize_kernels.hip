@@ -442,6 +442,21 @@ finalize_kernel(const FinalizeArgs a)
 
 // ------------------------------------------------------------ dispatch ---
 
+// Whether `vpt` can be chosen at all: once a value that fits every even n
+// (VPT 1) appears in MF_VPT_ORDER, later entries are never picked, so their
+// kernels are not instantiated.
+constexpr bool vpt_reachable(int vpt)
+{
+    constexpr int order[] = {MF_VPT_ORDER};
+    for (int v : order) {
+        if (v == vpt)
+            return true;
+        if (v == 1)
+            return false;
+    }
+    return false;
+}
+
 // Vectors per thread for hidden = 256 n: the first of MF_VPT_ORDER whose
 // team of 32 n / VPT threads is a whole number of waves within the launch
 // bound; 0 if none (then one vector per thread with the last half wave idle).
@@ -500,20 +515,24 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     const size_t lds = residency_lds(a.hidden, slots_in_flight(KC, vpt > 0 ? vpt : 1));
     switch (vpt) {
     case 8:
-        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid,
-                           dim3(nv / 8), lds, s, a);
+        if constexpr (vpt_reachable(8))
+            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid,
+                               dim3(nv / 8), lds, s, a);
         break;
     case 4:
-        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid,
-                           dim3(nv / 4), lds, s, a);
+        if constexpr (vpt_reachable(4))
+            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid,
+                               dim3(nv / 4), lds, s, a);
         break;
     case 2:
-        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid,
-                           dim3(nv / 2), lds, s, a);
+        if constexpr (vpt_reachable(2))
+            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid,
+                               dim3(nv / 2), lds, s, a);
         break;
     case 1:
-        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid,
-                           dim3(nv), lds, s, a);
+        if constexpr (vpt_reachable(1))
+            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid,
+                               dim3(nv), lds, s, a);
         break;
     default:   // n odd: 32 (n + 1) threads, the last half wave idle
         hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false>), grid,
