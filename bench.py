@@ -48,6 +48,10 @@ WORKLOADS = {
     "beam5": "token-major finalize + post RMSNorm: 16000 live of 16384, top-k 16, hidden 2048",
     "beam5_residual": "token-major finalize + post RMSNorm + residual add + next RMSNorm: "
                       "16000 of 16384 tokens, top-k 16, hidden 2048",
+    "imap7168": "index-map finalize+RMSNorm: 3000 tokens, hidden 7168, top-k 8, FP32 weights, "
+                "24000 rows grouped by expert (Zipf 1.1 over 256 experts)",
+    "imap2048k16": "index-map finalize+RMSNorm (weight before norm): 16000 tokens, hidden 2048, "
+                   "top-k 16, FP32 weights, 256000 rows grouped by expert (Zipf 1.1 over 256)",
 }
 
 

@@ -18,8 +18,9 @@
 //    wave reads 1 KiB contiguous runs of each gathered row;
 //  - the token's indices and weights are uniform, so they live in SGPRs and
 //    validity is a scalar branch: invalid slots issue no memory traffic;
-//  - up to 16 row vectors per thread (all of a token's rows for top-k 8,
-//    batches of 16 / VPT slots otherwise) are in flight before the first FMA;
+//  - up to 32 (index map) or 16 (token major) row vectors per thread are in
+//    flight before the first FMA: all of a token's rows at top-k 8, and at
+//    top-k 16 on the index map; larger top-k in batches;
 //  - the FP32 sum, the sum of squares and the normalised values stay in
 //    VGPRs; the cross-lane sum uses DPP row operations, the cross-wave sum
 //    one LDS exchange and barrier;
@@ -46,8 +47,15 @@
 #define MF_INFLIGHT_KB_PER_CU 96 // > 0: cap resident workgroups so that their row
                                  // loads in flight total about this much per CU
 #endif
-#ifndef MF_MAX_VECS
-#define MF_MAX_VECS 16          // row vectors in flight per thread
+// Row vectors in flight per thread.  Scattered index-map rows want every
+// slot in flight (top-k 16 at two vectors per thread: 14 % faster than two
+// batches of 8); a token-major token is one contiguous block, which is
+// faster fetched in halves (top-k 16: 10 % faster than all at once).
+#ifndef MF_MAX_VECS_INDEX_MAP
+#define MF_MAX_VECS_INDEX_MAP 32
+#endif
+#ifndef MF_MAX_VECS_TOKEN_MAJOR
+#define MF_MAX_VECS_TOKEN_MAJOR 16
 #endif
 #ifndef MF_VPT_ORDER
 #define MF_VPT_ORDER 2, 1, 4, 8 // preferred vectors per thread, first that fits
@@ -155,9 +163,17 @@ __device__ __forceinline__ float block_sum(float v, int bank = 0)
 // KC: top_k when known at compile time (0: read a.top_k).
 // VPT: 16-byte vectors per thread; EXACT: hidden/8 == blockDim.x * VPT.
 // Slots whose rows one workgroup has in flight at once (see finalize_kernel).
-constexpr int slots_in_flight(int kc, int vpt)
+// One vector per thread means teams of up to 1024 threads, whose launch
+// bound leaves 128 VGPRs per thread: at most 16 vectors (64 VGPRs) there.
+constexpr int max_vecs(Layout l, int vpt)
 {
-    return (kc > 0 && kc * vpt <= MF_MAX_VECS) ? kc : MF_MAX_VECS / vpt;
+    const int m = l == Layout::kIndexMap ? MF_MAX_VECS_INDEX_MAP : MF_MAX_VECS_TOKEN_MAJOR;
+    return vpt == 1 && m > 16 ? 16 : m;
+}
+
+constexpr int slots_in_flight(Layout l, int kc, int vpt)
+{
+    return (kc > 0 && kc * vpt <= max_vecs(l, vpt)) ? kc : max_vecs(l, vpt) / vpt;
 }
 
 template <int VPT>
@@ -167,9 +183,9 @@ template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
 __global__ void __launch_bounds__(max_team<VPT>())
 finalize_kernel(const FinalizeArgs a)
 {
-    // Slots whose rows are in flight together: MF_MAX_VECS / VPT, or all of
+    // Slots whose rows are in flight together: max_vecs(L, VPT) / VPT, or all of
     // them when a compile-time slot count fits.
-    constexpr int KB = slots_in_flight(KC, VPT);
+    constexpr int KB = slots_in_flight(L, KC, VPT);
     static_assert(KB >= 1 && (KC == 0 || KC % KB == 0), "slot batch must divide top_k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
@@ -512,7 +528,7 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     const int nv = 32 * n;
     const dim3 grid((unsigned)a.num_tokens);
     const int vpt = pick_vpt(n);
-    const size_t lds = residency_lds(a.hidden, slots_in_flight(KC, vpt > 0 ? vpt : 1));
+    const size_t lds = residency_lds(a.hidden, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
     switch (vpt) {
     case 8:
         if constexpr (vpt_reachable(8))

@@ -87,6 +87,8 @@ INDEX_CONFIGS = {
     "tiny_nan_rows": lambda: wl.tiny(nan_rows_beyond=2),
     "decode": lambda: wl.decode(poison=True),
     "prefill": lambda: wl.prefill(),
+    "imap7168": lambda: wl.imap7168(),
+    "imap2048k16": lambda: wl.imap2048k16(),
 }
 
 

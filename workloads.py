@@ -17,6 +17,9 @@ the finalize pages' parameter contracts imply:
   beam4    token major, capacity 4096, K=8,  H=7168, 3000 live, scale 2.5,
            no norm
   beam5    token major, capacity 16384, K=16, H=2048, 16000 live, post norm
+
+and, for the index-map path over the token-major path's envelope, the two
+beam shapes through an expert-grouped index map (imap7168, imap2048k16).
 """
 from __future__ import annotations
 
@@ -283,5 +286,28 @@ def beam5(**kw) -> TokenMajorCase:
     return make_token_major_case(4, **args)
 
 
+def imap7168(**kw) -> IndexMapCase:
+    """Index-map finalize+RMSNorm at the beam4 shape: 3000 tokens, hidden
+    7168, top-k 8, rows grouped by expert (Zipf 1.1 over 256 experts)."""
+    args = dict(num_tokens=3000, hidden=7168, top_k=8, weights_dtype="fp32", logit_std=2.0,
+                grouping="zipf", num_experts=256, zipf_s=1.1, eps=1e-6, gain_center=1.0,
+                weight_before_norm=False, norm_weight_mean=0.0, norm_weight_std=0.1,
+                name="imap7168")
+    args.update(kw)
+    return make_index_map_case(5, **args)
+
+
+def imap2048k16(**kw) -> IndexMapCase:
+    """Index-map finalize+RMSNorm at the beam5 shape: 16000 tokens, hidden
+    2048, top-k 16, rows grouped by expert (Zipf 1.1 over 256 experts)."""
+    args = dict(num_tokens=16000, hidden=2048, top_k=16, weights_dtype="fp32",
+                logit_std=1.0, grouping="zipf", num_experts=256, zipf_s=1.1, eps=1e-6,
+                gain_center=0.0, weight_before_norm=True, norm_weight_mean=1.0,
+                norm_weight_std=0.1, name="imap2048k16")
+    args.update(kw)
+    return make_index_map_case(6, **args)
+
+
 CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill,
-           "beam4": beam4, "beam5": beam5}
+           "beam4": beam4, "beam5": beam5, "imap7168": imap7168,
+           "imap2048k16": imap2048k16}
