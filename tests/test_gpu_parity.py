@@ -400,6 +400,39 @@ def test_zero_rows_launch_nothing():
     assert np.all(host_bits(out) == 0x1234)
 
 
+def test_row_offsets_beyond_2_gib():
+    """Rows whose byte offset exceeds 2^31 (70000 rows x 32 KiB stride,
+    2.3 GB): the gather addresses them with 64-bit offsets.  The oracle gets
+    the same rows compacted and the index map remapped accordingly."""
+    R, S, H, T, K = 70000, 16384, 4096, 24, 8
+    rng = np.random.Generator(np.random.PCG64(123))
+    picked = np.sort(rng.choice(np.arange(R - 4000, R), size=T * K, replace=False))
+    assert int(picked[0]) * S * 2 > 2 ** 31
+    rows = wl.normal_bf16(rng, (T * K, H))
+    order = rng.permutation(T * K)
+    idx_small = order.reshape(T, K).astype(np.int32)            # into the compact rows
+    idx_big = picked[order].reshape(T, K).astype(np.int32)      # into the big matrix
+    idx_small[0, 3] = -1
+    idx_big[0, 3] = -1
+    w = wl.softmax_rows(rng.standard_normal((T, K)))
+    nw = wl.normal_bf16(rng, (H,), std=0.1)
+    big = torch.full((R, S), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big[torch.from_numpy(picked).cuda(), :H] = dev_bf16(rows)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    mf.moe_finalize_rmsnorm(big, torch.from_numpy(w).cuda(), torch.from_numpy(idx_big).cuda(),
+                            dev_bf16(nw), out, eps=1e-6, gain_center=1.0,
+                            weight_before_norm=False)
+    out2 = torch.empty_like(out)
+    mf.moe_finalize(big, torch.from_numpy(w).cuda(), torch.from_numpy(idx_big).cuda(), out2)
+    sync()
+    want = oracle.moe_finalize_rmsnorm(rows, w, idx_small, nw, eps=1e-6, gain_center=1.0,
+                                       weight_before_norm=False)
+    assert_within_ulp(host_bits(out), want, 1, NORM_MIN_EXACT, "rows past 2 GiB, norm")
+    assert_bits_equal(host_bits(out2), oracle.moe_finalize(rows, w, idx_small, H),
+                      "rows past 2 GiB, finalize")
+    del big
+
+
 def test_live_equals_capacity_and_partial_live():
     c = wl.make_token_major_case(77, capacity=40, top_k=8, hidden=7168, live_tokens=40,
                                  routed_scale=2.5)
