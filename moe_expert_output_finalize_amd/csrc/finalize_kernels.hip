@@ -25,7 +25,8 @@
 //    VGPRs; the cross-lane sum uses DPP row operations, the cross-wave sum
 //    one LDS exchange and barrier;
 //  - BF16 rounding is the CDNA4 packed convert (nearest even), two values
-//    per instruction, and results leave as 16-byte stores;
+//    per instruction, and results leave as 16-byte buffer stores through a
+//    resource spanning the output row, with device-scope cache policy;
 //  - workgroup b takes token b: consecutive tokens run at the same time on
 //    the eight XCDs (workgroups are dispatched to them in turn), so rows of
 //    one expert that sit next to each other in memory are fetched together.
@@ -40,8 +41,12 @@
 #ifndef MF_NONTEMPORAL_ROWS
 #define MF_NONTEMPORAL_ROWS 1   // gathered rows are read exactly once
 #endif
-#ifndef MF_NONTEMPORAL_OUT
-#define MF_NONTEMPORAL_OUT 1    // output rows are written exactly once
+// Cache-policy operand of the output stores (CDNA4 buffer store: bit 0 sc0,
+// bit 1 nt, bit 4 sc1).  Device-scope sc1 stores measured 1.5-2 % faster
+// than non-temporal ones and 6 % faster than the default policy, with the
+// gathered rows still read non-temporally.
+#ifndef MF_STORE_POLICY
+#define MF_STORE_POLICY 16
 #endif
 #ifndef MF_INFLIGHT_KB_PER_CU
 #define MF_INFLIGHT_KB_PER_CU 96 // > 0: cap resident workgroups so that their row
@@ -102,13 +107,19 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 #endif
 }
 
-__device__ __forceinline__ void store_out_vec(u32x4 *p, const u32x4 &v)
+// Buffer resource word 3 for raw (unformatted, unswizzled) access on gfx9.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Resource spanning one output row of `bytes` bytes (uniform per workgroup).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_resource(uint16_t *row, uint32_t bytes)
 {
-#if MF_NONTEMPORAL_OUT
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    return __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)bytes, kRawBufferWord3);
+}
+
+__device__ __forceinline__ void store_out_vec(__amdgpu_buffer_rsrc_t row, uint32_t byte_off,
+                                              const u32x4 &v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, row, byte_off, 0, MF_STORE_POLICY);
 }
 
 template <bool BF16>
@@ -290,11 +301,12 @@ finalize_kernel(const FinalizeArgs a)
         }
     }
 
-    uint16_t *out_row = a.out + t * (int64_t)a.hidden;
+    const __amdgpu_buffer_rsrc_t out_row =
+        row_resource(a.out + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
     auto store = [&](int i, const u32x4 &o) {
         const int j = lane + i * team;
         if (EXACT || j < nv)
-            store_out_vec(reinterpret_cast<u32x4 *>(out_row) + j, o);
+            store_out_vec(out_row, (uint32_t)j * 16u, o);
     };
 
     if constexpr (EPI == Epilogue::kRound) {
@@ -391,7 +403,8 @@ finalize_kernel(const FinalizeArgs a)
                 ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
         ss = block_sum(ss, 1);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps2);
-        uint16_t *out2_row = a.out2 + t * (int64_t)a.hidden;
+        const __amdgpu_buffer_rsrc_t out2_row =
+            row_resource(a.out2 + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             u32x4 o;
@@ -406,7 +419,7 @@ finalize_kernel(const FinalizeArgs a)
             }
             const int j = lane + i * team;
             if (EXACT || j < nv)
-                store_out_vec(reinterpret_cast<u32x4 *>(out2_row) + j, o);
+                store_out_vec(out2_row, (uint32_t)j * 16u, o);
         }
         return;
     }
