@@ -479,6 +479,53 @@ def test_hardware_bf16_rounding_matches_round_to_nearest_even():
     assert_bits_equal(gpu_finalize(IndexMapOnDevice(im)), oracle_finalize(im), "finalize bf16(w)")
 
 
+def test_graph_capture_and_replay():
+    """The entry points allocate, synchronise and memset nothing, so they can
+    be captured in a HIP graph: every replay (with eager work and
+    synchronisation between replays) must equal the eager launch."""
+    c = wl.tiny(num_tokens=64, num_rows=512, invalid_frac=0.05)
+    d = IndexMapOnDevice(c)
+    b = wl.make_token_major_case(9, capacity=48, top_k=8, hidden=2048, live_tokens=40,
+                                 routed_scale=1.5, post_eps=1e-6, post_weight_std=0.05)
+    bd = TokenMajorOnDevice(b)
+    rng = np.random.Generator(np.random.PCG64(10))
+    res = dev_bf16(wl.normal_bf16(rng, (40, 2048)))
+    nw = dev_bf16(wl.normal_bf16(rng, (2048,), mean=1.0, std=0.1))
+    out = d.new_output()
+    h = torch.empty((40, 2048), dtype=torch.bfloat16, device="cuda")
+    n = torch.empty_like(h)
+
+    def launch():
+        mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, out, eps=c.eps,
+                                gain_center=c.gain_center, weight_before_norm=False)
+        mf.beam_moe_finalize_norm_residual_norm(bd.expert_outputs, bd.weights, res,
+                                                bd.post_weight, b.post_eps, nw, 1e-6, None,
+                                                b.routed_scale, hidden_out=h, normalized_out=n)
+
+    launch()                       # eager (also warms every lazily queried attribute)
+    sync()
+    want = (host_bits(out), host_bits(h), host_bits(n))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch()
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    for rep in range(3):
+        out.fill_(0.0)
+        h.fill_(0.0)
+        n.fill_(0.0)
+        sync()
+        g.replay()
+        sync()
+        got = (host_bits(out), host_bits(h), host_bits(n))
+        for name, x, y in zip(("rmsnorm", "hidden", "normalized"), got, want):
+            assert_bits_equal(x, y, f"graph replay {rep} {name}")
+
+
 def test_runs_on_the_given_stream():
     c = wl.tiny(num_tokens=32, num_rows=256)
     d = IndexMapOnDevice(c)
