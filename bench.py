@@ -69,6 +69,9 @@ def parse_args():
                    help="skip timing the CPU oracle (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle sample")
+    p.add_argument("--graph", action="store_true",
+                   help="capture the timed steps in one HIP graph and replay it (for "
+                        "launch-bound small workloads)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -352,15 +355,34 @@ def main():
 
     # Timed region: K back-to-back launches on the current stream, bracketed
     # by synchronisation (wall clock) and by one pair of HIP events recorded
-    # on that same stream (kernel time per launch = event span / K).
+    # on that same stream (kernel time per launch = event span / K).  With
+    # --graph the K launches are captured once in a HIP graph and the timed
+    # region is one replay of it.
     K = args.steps
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            bench.step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                bench.step(args.warmup + i)
+        graph.replay()
+        torch.cuda.synchronize()
     ev_start = torch.cuda.Event(enable_timing=True)
     ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev_start.record()
-    for i in range(K):
-        bench.step(args.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            bench.step(args.warmup + i)
     ev_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -389,6 +411,7 @@ def main():
         cpu = cpu_baseline(bench, args.cpu_seconds)
 
     config = {"workload": WORKLOADS[args.config], "name": args.config,
+              "launch": "hip_graph" if args.graph else "stream",
               "tokens_per_step": bench.tokens, "algorithmic_bytes_per_step": bench.bytes,
               "rotating_buffer_sets": bench.sets, "io_dtype": "bf16"}
     if isinstance(c, wl.IndexMapCase):

@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "launch.hpp"
 
@@ -509,23 +510,26 @@ inline int pick_vpt(int n)
 inline size_t residency_lds(int hidden, int slots)
 {
 #if MF_INFLIGHT_KB_PER_CU > 0
-    struct Limits { int per_cu, per_block; };
-    static Limits lim[64];
+    // Per-device LDS limits, queried once; concurrent first calls store the
+    // same values.
+    static std::atomic<int> lds_per_cu[64], lds_per_block[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 0;
-    if (lim[dev].per_cu == 0) {
-        int cu = 0, blk = 0;
+    int cu = lds_per_cu[dev].load(std::memory_order_relaxed);
+    int blk = lds_per_block[dev].load(std::memory_order_relaxed);
+    if (cu <= 0 || blk <= 0) {
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
                 hipSuccess || cu <= 0 || blk <= 0)
             return 0;
-        lim[dev] = {cu, blk};
+        lds_per_cu[dev].store(cu, std::memory_order_relaxed);
+        lds_per_block[dev].store(blk, std::memory_order_relaxed);
     }
     const int64_t per_block = 2LL * hidden * slots;           // row bytes in flight
     const int64_t blocks = std::max<int64_t>(2, (int64_t)MF_INFLIGHT_KB_PER_CU * 1024 / per_block);
-    const int64_t lds = std::min<int64_t>(lim[dev].per_cu / blocks - 1024, lim[dev].per_block);
+    const int64_t lds = std::min<int64_t>(cu / blocks - 1024, blk);
     return lds > 0 ? (size_t)lds : 0;
 #else
     (void)hidden;
