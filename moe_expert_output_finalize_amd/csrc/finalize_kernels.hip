@@ -66,6 +66,14 @@
 #ifndef MF_VPT_ORDER
 #define MF_VPT_ORDER 2, 1, 4, 8 // preferred vectors per thread, first that fits
 #endif
+// Index-map rows up to this hidden size take one vector per thread instead
+// (teams of up to 512 threads): 1 % faster at 8192 tokens and hidden 4096,
+// 5 % at 256 tokens, 3 % at hidden 2048 / top-k 16; at hidden 7168 the
+// 896-thread teams are 5 % slower, and token-major tokens prefer two
+// vectors per thread at every size measured.  0 disables the override.
+#ifndef MF_INDEX_MAP_VPT1_MAX_HIDDEN
+#define MF_INDEX_MAP_VPT1_MAX_HIDDEN 4096
+#endif
 
 namespace mf {
 namespace {
@@ -487,11 +495,15 @@ constexpr bool vpt_reachable(int vpt)
     return false;
 }
 
-// Vectors per thread for hidden = 256 n: the first of MF_VPT_ORDER whose
+// Vectors per thread for hidden = 256 n: one for index-map rows up to
+// MF_INDEX_MAP_VPT1_MAX_HIDDEN, else the first of MF_VPT_ORDER whose
 // team of 32 n / VPT threads is a whole number of waves within the launch
 // bound; 0 if none (then one vector per thread with the last half wave idle).
-inline int pick_vpt(int n)
+inline int pick_vpt(Layout l, int n)
 {
+    if (l == Layout::kIndexMap && 256 * n <= MF_INDEX_MAP_VPT1_MAX_HIDDEN && n % 2 == 0 &&
+        vpt_reachable(1))
+        return 1;
     for (int vpt : {MF_VPT_ORDER}) {
         const int team = 32 * n / vpt;
         const int bound = vpt == 1 ? 1024 : vpt == 2 ? 512 : 256;
@@ -544,7 +556,7 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     const int n = a.hidden / 256;
     const int nv = 32 * n;
     const dim3 grid((unsigned)a.num_tokens);
-    const int vpt = pick_vpt(n);
+    const int vpt = pick_vpt(L, n);
     const size_t lds = residency_lds(a.hidden, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
     switch (vpt) {
     case 8:
