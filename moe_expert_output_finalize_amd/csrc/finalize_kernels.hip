@@ -179,18 +179,17 @@ __device__ __forceinline__ float block_sum(float v, int bank = 0)
 
 // ------------------------------------------------------------ kernel -----
 
-// L: where slot rows come from (index map, token major, or one row per token).
-// KC: top_k when known at compile time (0: read a.top_k).
-// VPT: 16-byte vectors per thread; EXACT: hidden/8 == blockDim.x * VPT.
-// Slots whose rows one workgroup has in flight at once (see finalize_kernel).
-// One vector per thread means teams of up to 1024 threads, whose launch
-// bound leaves 128 VGPRs per thread: at most 16 vectors (64 VGPRs) there.
+// Row vectors one thread keeps in flight.  One vector per thread means teams
+// of up to 1024 threads, whose launch bound leaves 128 VGPRs per thread: at
+// most 16 vectors (64 VGPRs) there.
 constexpr int max_vecs(Layout l, int vpt)
 {
     const int m = l == Layout::kIndexMap ? MF_MAX_VECS_INDEX_MAP : MF_MAX_VECS_TOKEN_MAJOR;
     return vpt == 1 && m > 16 ? 16 : m;
 }
 
+// Slots whose rows one workgroup has in flight at once: all of them when a
+// compile-time slot count fits, else batches of max_vecs / VPT.
 constexpr int slots_in_flight(Layout l, int kc, int vpt)
 {
     return (kc > 0 && kc * vpt <= max_vecs(l, vpt)) ? kc : max_vecs(l, vpt) / vpt;
@@ -199,12 +198,16 @@ constexpr int slots_in_flight(Layout l, int kc, int vpt)
 template <int VPT>
 constexpr int max_team() { return VPT == 1 ? 1024 : VPT == 2 ? 512 : 256; }
 
+// One workgroup finalizes token blockIdx.x.
+//   L      where slot rows come from (index map, token major, one row per token)
+//   W_BF16 weights are BF16 (else FP32)
+//   EPI    what follows the FP32 routed sum
+//   KC     top_k when known at compile time (0: read a.top_k)
+//   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
 template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
 __global__ void __launch_bounds__(max_team<VPT>())
 finalize_kernel(const FinalizeArgs a)
 {
-    // Slots whose rows are in flight together: max_vecs(L, VPT) / VPT, or all of
-    // them when a compile-time slot count fits.
     constexpr int KB = slots_in_flight(L, KC, VPT);
     static_assert(KB >= 1 && (KC == 0 || KC % KB == 0), "slot batch must divide top_k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||

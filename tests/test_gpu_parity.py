@@ -526,6 +526,37 @@ def test_graph_capture_and_replay():
             assert_bits_equal(x, y, f"graph replay {rep} {name}")
 
 
+def test_concurrent_streams_match_serial_results():
+    """Different entry points running at the same time on two streams give
+    the results they give alone (no shared state in the library)."""
+    c = wl.tiny(num_tokens=512, num_rows=4096, invalid_frac=0.02)
+    d = IndexMapOnDevice(c)
+    b = wl.make_token_major_case(12, capacity=600, top_k=16, hidden=2048, live_tokens=600,
+                                 routed_scale=1.0, post_eps=1e-6, post_weight_std=0.05)
+    bd = TokenMajorOnDevice(b)
+    o1, o2 = d.new_output(), bd.new_output()
+    mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, o1, eps=c.eps,
+                            gain_center=c.gain_center, weight_before_norm=False)
+    mf.beam_moe_finalize(bd.expert_outputs, bd.weights, o2, 1.0, bd.post_weight, 1e-6)
+    sync()
+    want1, want2 = host_bits(o1), host_bits(o2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        p1, p2 = d.new_output(), bd.new_output()
+        sync()
+        with torch.cuda.stream(s1):
+            mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, p1, eps=c.eps,
+                                    gain_center=c.gain_center, weight_before_norm=False)
+        with torch.cuda.stream(s2):
+            mf.beam_moe_finalize(bd.expert_outputs, bd.weights, p2, 1.0, bd.post_weight, 1e-6)
+        outs.append((p1, p2))
+    sync()
+    for p1, p2 in outs:
+        assert_bits_equal(host_bits(p1), want1, "stream 1")
+        assert_bits_equal(host_bits(p2), want2, "stream 2")
+
+
 def test_runs_on_the_given_stream():
     c = wl.tiny(num_tokens=32, num_rows=256)
     d = IndexMapOnDevice(c)
