@@ -80,8 +80,8 @@ enum mf_dtype {
  *
  * For token t < num_tokens and slot k < top_k, i = expanded_idx_to_permuted_idx
  * [t*top_k + k] names row i of gemm2_permuted; an index outside [0, num_rows)
- * contributes nothing (its row and weight are not read, the other weights are
- * not rescaled).  With acc the FP32 weighted sum of the valid rows' first
+ * contributes nothing (no row is read for it, its weight is not used, and the
+ * other weights are not rescaled).  With acc the FP32 weighted sum of the valid rows' first
  * `hidden` columns and g[h] = float(norm_weight[h]) + gain_center (FP32 add):
  *   weight_before_norm == 0:  out = acc / sqrt(mean(acc^2) + eps) * g
  *   weight_before_norm != 0:  z = acc * g;  out = z / sqrt(mean(z^2) + eps)
@@ -103,7 +103,8 @@ enum mf_dtype {
  *                   [BEAM] for the index map too.
  *   eps             added to the mean square inside the square root.
  *
- * Errors: NULL pointer (any, when num_tokens > 0) -> MF_ERR_NULL_POINTER;
+ * Errors: NULL pointer when num_tokens > 0 (gemm2_permuted may be NULL when
+ * num_rows == 0: every index is then invalid) -> MF_ERR_NULL_POINTER;
  * hidden or top_k outside the envelope, num_tokens < 0 or > INT32_MAX, num_rows < 0,
  * row_stride < hidden -> MF_ERR_BAD_SHAPE; bad weights_dtype
  * -> MF_ERR_BAD_DTYPE; misaligned pointer or row_stride % 8 != 0 ->
