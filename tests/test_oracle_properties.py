@@ -60,16 +60,16 @@ def test_power_of_two_weight_scaling_commutes(case):
 @SETTINGS
 @given(index_cases())
 def test_norm_output_rms(case):
-    """With the weight before the norm, the output RMS is 1 up to eps and
-    BF16 rounding for any token with a nonzero sum."""
+    """With the weight before the norm and a negligible eps, the output RMS is
+    1 up to BF16 rounding for any token whose sum is not tiny."""
     g, R, H, idx, w, rng = case
     nw = wl.normal_bf16(rng, (H,), mean=1.0, std=0.2)
-    out = oracle.moe_finalize_rmsnorm(g, w, idx, nw, eps=1e-9, gain_center=0.0,
+    out = oracle.moe_finalize_rmsnorm(g, w, idx, nw, eps=1e-30, gain_center=0.0,
                                       weight_before_norm=True, num_rows=R)
     acc = oracle.routed_sum(g, w, idx, H, num_rows=R)
     y = wl.bf16_bits_to_f32(out).astype(np.float64)
     for t in range(idx.shape[0]):
-        if np.abs(acc[t]).max() > 1e-3:
+        if np.abs(acc[t]).max() > 1e-2:
             rms = np.sqrt(np.mean(y[t] ** 2))
             assert abs(rms - 1.0) < 1e-2
 
