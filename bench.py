@@ -144,6 +144,7 @@ class IndexMapBench:
     def unfused_parts(self):
         c, torch = self.c, self.torch
         mids = [torch.empty_like(o) for o in self.outs]
+        outs = [torch.empty_like(o) for o in self.outs]
 
         def finalize(i):
             s = i % self.sets
@@ -151,7 +152,7 @@ class IndexMapBench:
 
         def norm(i):
             s = i % self.sets
-            self.mf.mf_rmsnorm(mids[s], self.nw, self.outs[s], eps=c.eps,
+            self.mf.mf_rmsnorm(mids[s], self.nw, outs[s], eps=c.eps,
                                gain_center=c.gain_center,
                                weight_before_norm=c.weight_before_norm)
         extra = 2 * c.num_tokens * c.hidden * 2
@@ -159,9 +160,12 @@ class IndexMapBench:
 
     def cpu_oracle(self, oracle, tokens: slice):
         c = self.c
-        oracle.moe_finalize_rmsnorm(c.gemm2, c.expert_weights[tokens], c.idx[tokens],
-                                    c.norm_weight, eps=c.eps, gain_center=c.gain_center,
-                                    weight_before_norm=c.weight_before_norm)
+        return [oracle.moe_finalize_rmsnorm(c.gemm2, c.expert_weights[tokens], c.idx[tokens],
+                                            c.norm_weight, eps=c.eps, gain_center=c.gain_center,
+                                            weight_before_norm=c.weight_before_norm)]
+
+    def gpu_outputs(self):
+        return [self.outs[0]]
 
 
 class TokenMajorBench:
@@ -190,8 +194,11 @@ class TokenMajorBench:
     def cpu_oracle(self, oracle, tokens: slice):
         c = self.c
         n = len(range(*tokens.indices(c.live_tokens)))
-        oracle.beam_moe_finalize(c.expert_outputs[tokens], c.expert_weights[tokens], n,
-                                 c.routed_scale, c.post_weight, c.post_eps)
+        return [oracle.beam_moe_finalize(c.expert_outputs[tokens], c.expert_weights[tokens], n,
+                                         c.routed_scale, c.post_weight, c.post_eps)]
+
+    def gpu_outputs(self):
+        return [self.outs[0]]
 
 
 def time_launches(torch, fns, steps: int, warmup: int):
@@ -248,6 +255,8 @@ class ResidualBench(TokenMajorBench):
     def unfused_parts(self):
         c, torch = self.c, self.torch
         mids = [torch.empty_like(o) for o in self.outs]
+        hid = [torch.empty_like(o) for o in self.outs]
+        nrm = [torch.empty_like(o) for o in self.outs]
 
         def finalize(i):
             s = i % self.sets
@@ -257,37 +266,76 @@ class ResidualBench(TokenMajorBench):
         def consumer(i):
             s = i % self.sets
             self.mf.beam_norm_residual_norm(mids[s], self.res, None, None, self.nw,
-                                            self.next_eps, None, hidden_out=self.outs[s],
-                                            normalized_out=self.outs2[s])
+                                            self.next_eps, None, hidden_out=hid[s],
+                                            normalized_out=nrm[s])
         extra = 2 * c.live_tokens * c.hidden * 2
         return [("beam_moe_finalize", finalize), ("beam_norm_residual_norm", consumer)], \
             self.bytes + extra
 
     def cpu_oracle(self, oracle, tokens: slice):
         c = self.c
-        n = len(range(*tokens.indices(c.live_tokens)))
-        oracle.beam_moe_finalize_norm_residual_norm(
+        return list(oracle.beam_moe_finalize_norm_residual_norm(
             c.expert_outputs[tokens], c.expert_weights[tokens], self.res_host[tokens],
-            c.post_weight, c.post_eps, self.nw_host, self.next_eps, None, c.routed_scale)
+            c.post_weight, c.post_eps, self.nw_host, self.next_eps, None, c.routed_scale))
+
+    def gpu_outputs(self):
+        return [self.outs[0], self.outs2[0]]
+
+    agreement_note = ("hidden = y + residual after a post-norm: where the two nearly cancel, "
+                      "the one-ulp freedom of the post-normed y is many ulps of hidden; "
+                      "the parity tests check y, the consumer and fused == unfused separately")
+
+
+def bf16_ulp_distance(a, b):
+    """Distance in BF16 grid steps between two uint16 bit-pattern arrays
+    (+0 == -0; NaN vs NaN is 0, NaN vs a number is 2^20)."""
+    import numpy as np
+    a = a.astype(np.int64)
+    b = b.astype(np.int64)
+
+    def ordered(v):
+        return np.where(v & 0x8000, -(v & 0x7FFF), v & 0x7FFF)
+
+    d = np.abs(ordered(a) - ordered(b))
+    na = ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)
+    nb = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    return np.where(na | nb, np.where(na & nb, 0, 1 << 20), d)
 
 
 def cpu_baseline(bench, seconds: float) -> dict:
     """The oracle (single-threaded C) on whole passes over the workload's
-    tokens, repeated until `seconds` of CPU time have been spent."""
+    tokens, repeated until `seconds` of CPU time have been spent.  Its output
+    is also compared with what the timed GPU steps wrote."""
+    import numpy as np
     import oracle
     oracle.build()
     T = bench.tokens
     reps, t0 = 0, time.perf_counter()
+    first = None
     while True:
-        bench.cpu_oracle(oracle, slice(0, T))
+        out = bench.cpu_oracle(oracle, slice(0, T))
+        first = out if first is None else first
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    worst, exact, within1, n = 0, 0, 0, 0
+    for want, got_t in zip(first, bench.gpu_outputs()):
+        got = got_t.cpu().view(bench.torch.int16).numpy().view(np.uint16)
+        d = bf16_ulp_distance(got, want)
+        worst = max(worst, int(d.max()))
+        exact += int((d == 0).sum())
+        within1 += int((d <= 1).sum())
+        n += d.size
+    agree = {"max_ulp": worst, "bit_exact_fraction": exact / max(n, 1),
+             "within_1_ulp_fraction": within1 / max(n, 1), "elements": n}
+    if getattr(bench, "agreement_note", None):
+        agree["note"] = bench.agreement_note
     return {"value": reps * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full pass(es) over all {T} tokens of the same workload, "
                       f"single thread, {el:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu": cpu_model()}
+            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu": cpu_model(),
+            "gpu_vs_oracle": agree}
 
 
 def cpu_model() -> str:
