@@ -370,9 +370,10 @@ def copy_ceiling(torch, mib: int = 1024, reps: int = 10) -> float:
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the finalize runs on one GPU's share of the tokens; see DESIGN.md for "
-              "how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
+              "the finalize is per token and needs no communication, so each GPU runs "
+              "it on its own share of the tokens and the one-GPU figure is that share's",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
