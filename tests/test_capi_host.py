@@ -185,3 +185,13 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         mf.moe_finalize(g, torch.zeros(1, 8), torch.zeros(1, 8, dtype=torch.int32),
                         torch.zeros(1, 256, dtype=torch.bfloat16))
+
+
+def test_c_driver_links_against_the_library():
+    """The plain-C driver of the GPU tests resolves libmoe_finalize.so and the
+    HIP runtime; without arguments it prints its usage before any HIP call."""
+    import subprocess
+    driver = os.path.join(ROOT, "tests", "capi_c_driver")
+    assert os.path.exists(driver), "run __graft_entry__.build() first"
+    r = subprocess.run([driver], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage:" in r.stderr
