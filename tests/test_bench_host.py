@@ -87,3 +87,18 @@ def test_stored_traffic_requires_matching_sources(monkeypatch):
     assert bench.stored_traffic("prefill") is None
     assert bench.stored_traffic("no_such_workload") is None
 
+
+
+def test_threaded_oracle_baseline_covers_every_token():
+    """The all-cores CPU baseline splits the tokens into contiguous slices;
+    the slices' outputs put together equal one pass over all tokens."""
+    import oracle
+    import workloads as wl
+    c = wl.tiny(num_tokens=37, num_rows=37 * 8, invalid_frac=0.1)
+    fake = SimpleNamespace(c=c, tokens=c.num_tokens)
+    fake.cpu_oracle = lambda orc, sl: bench.IndexMapBench.cpu_oracle(fake, orc, sl)
+    rec = bench.cpu_baseline_threads(fake, oracle, 0.0)
+    assert rec["cores"] >= 1 and rec["value"] > 0 and rec["unit"] == "tokens/s"
+    whole = fake.cpu_oracle(oracle, slice(0, 37))[0]
+    parts = [fake.cpu_oracle(oracle, slice(a, b))[0] for a, b in ((0, 5), (5, 20), (20, 37))]
+    assert np.array_equal(np.concatenate(parts), whole)
