@@ -188,10 +188,18 @@ constexpr int max_vecs(Layout l, int vpt)
     return vpt == 1 && m > 16 ? 16 : m;
 }
 
+// Slot-count template argument for a top-k read at run time that is at most
+// 8: the kernel is sized like the top-k 8 one (registers for 8 slots), so
+// small top-k keeps the occupancy of the common case.
+constexpr int kSmallTopK = -1;
+
 // Slots whose rows one workgroup has in flight at once: all of them when a
-// compile-time slot count fits, else batches of max_vecs / VPT.
+// compile-time slot count fits, 8 (or what fits) for a small run-time top-k,
+// else batches of max_vecs / VPT.
 constexpr int slots_in_flight(Layout l, int kc, int vpt)
 {
+    if (kc == kSmallTopK)
+        return 8 * vpt <= max_vecs(l, vpt) ? 8 : max_vecs(l, vpt) / vpt;
     return (kc > 0 && kc * vpt <= max_vecs(l, vpt)) ? kc : max_vecs(l, vpt) / vpt;
 }
 
@@ -202,14 +210,15 @@ constexpr int max_team() { return VPT == 1 ? 1024 : VPT == 2 ? 512 : 256; }
 //   L      where slot rows come from (index map, token major, one row per token)
 //   W_BF16 weights are BF16 (else FP32)
 //   EPI    what follows the FP32 routed sum
-//   KC     top_k when known at compile time (0: read a.top_k)
+//   KC     top_k when known at compile time (0: read a.top_k; kSmallTopK:
+//          read a.top_k, which is at most 8)
 //   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
 template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
 __global__ void __launch_bounds__(max_team<VPT>())
 finalize_kernel(const FinalizeArgs a)
 {
     constexpr int KB = slots_in_flight(L, KC, VPT);
-    static_assert(KB >= 1 && (KC == 0 || KC % KB == 0), "slot batch must divide top_k");
+    static_assert(KB >= 1 && (KC <= 0 || KC % KB == 0), "slot batch must divide top_k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
     constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
@@ -265,25 +274,24 @@ finalize_kernel(const FinalizeArgs a)
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
             const int k = k0 + b;
+            // Slots past a run-time top-k re-read the token's last slot
+            // (always in bounds) and are masked: the metadata loads stay
+            // unconditional, so they issue together behind one wait.
             const bool live = KC > 0 || k < top_k;
-            ok[b] = false;
-            w[b] = 0.0f;
-            row_off[b] = 0;
-            if (live) {
-                if constexpr (L == Layout::kIndexMap) {
-                    w[b] = load_weight<W_BF16>(a.weights, tk + k);
-                    const int32_t i = a.idx[tk + k];
-                    ok[b] = i >= 0 && (int64_t)i < a.num_rows;
-                    row_off[b] = (int64_t)i * a.row_stride;
-                } else if constexpr (L == Layout::kTokenMajor) {
-                    w[b] = load_weight<W_BF16>(a.weights, tk + k);
-                    ok[b] = true;
-                    row_off[b] = (tk + k) * (int64_t)a.hidden;
-                } else {   // kDirect: fma(1, x, +0) == x exactly
-                    w[b] = 1.0f;
-                    ok[b] = true;
-                    row_off[b] = t * a.row_stride;
-                }
+            const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
+            if constexpr (L == Layout::kIndexMap) {
+                w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                const int32_t i = a.idx[tk + kk];
+                ok[b] = live && i >= 0 && (int64_t)i < a.num_rows;
+                row_off[b] = (int64_t)i * a.row_stride;
+            } else if constexpr (L == Layout::kTokenMajor) {
+                w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                ok[b] = live;
+                row_off[b] = (tk + kk) * (int64_t)a.hidden;
+            } else {   // kDirect: fma(1, x, +0) == x exactly
+                w[b] = 1.0f;
+                ok[b] = live;
+                row_off[b] = t * a.row_stride;
             }
         }
         u32x4 v[KB][VPT];
@@ -560,7 +568,10 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     const int nv = 32 * n;
     const dim3 grid((unsigned)a.num_tokens);
     const int vpt = pick_vpt(L, n);
-    const size_t lds = residency_lds(a.hidden, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
+    // Slots actually in flight: with top-k read at run time the batch may be
+    // larger than top-k, and the cap must follow the rows really fetched.
+    const int slots = std::min(KC > 0 ? KC : a.top_k, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
+    const size_t lds = residency_lds(a.hidden, slots);
     switch (vpt) {
     case 8:
         if constexpr (vpt_reachable(8))
@@ -590,7 +601,8 @@ hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-// Compile-time slot counts for the common top-k values, runtime otherwise.
+// Compile-time slot counts for the common top-k values; other top-k read at
+// run time, by a kernel sized for 8 slots up to 8, in batches beyond.
 template <Layout L, bool W_BF16, Epilogue EPI>
 hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
 {
@@ -600,7 +612,8 @@ hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
     case 16:
         return launch_shape<L, W_BF16, EPI, 16>(a, s);
     default:
-        return launch_shape<L, W_BF16, EPI, 0>(a, s);
+        return a.top_k < 8 ? launch_shape<L, W_BF16, EPI, kSmallTopK>(a, s)
+                           : launch_shape<L, W_BF16, EPI, 0>(a, s);
     }
 }
 
