@@ -50,8 +50,8 @@
 #define MF_STORE_POLICY 16
 #endif
 #ifndef MF_INFLIGHT_KB_PER_CU
-#define MF_INFLIGHT_KB_PER_CU 96 // > 0: cap resident workgroups so that their row
-                                 // loads in flight total about this much per CU
+#define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
+                                  // loads in flight total about this much per CU
 #endif
 // Row vectors in flight per thread.  Scattered index-map rows want every
 // slot in flight (top-k 16 at two vectors per thread: 14 % faster than two
@@ -83,6 +83,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+constexpr int kMaxTopK = 32;   // the entry points reject larger top-k
+// s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kMaxWaves = 16;
 
 // ------------------------------------------------------------ BF16 -------
@@ -188,19 +191,23 @@ constexpr int max_vecs(Layout l, int vpt)
     return vpt == 1 && m > 16 ? 16 : m;
 }
 
-// Slot-count template argument for a top-k read at run time that is at most
-// 8: the kernel is sized like the top-k 8 one (registers for 8 slots), so
-// small top-k keeps the occupancy of the common case.
-constexpr int kSmallTopK = -1;
+// Slot-count template argument for a top-k read at run time:
+//   KC > 0   top-k is KC;
+//   KC == 0  any top-k, in batches of max_vecs / VPT slots;
+//   KC < 0   top-k at most -KC, registers sized for -KC slots, so a small
+//            top-k keeps a small register footprint and high occupancy.
+constexpr int small_topk_kc(int top_k) { return top_k <= 2 ? -2 : top_k <= 4 ? -4 : -8; }
 
-// Slots whose rows one workgroup has in flight at once: all of them when a
-// compile-time slot count fits, 8 (or what fits) for a small run-time top-k,
-// else batches of max_vecs / VPT.
+// Slots whose rows one workgroup has in flight at once: all of them when
+// they fit, else batches of max_vecs / VPT; a run-time top-k above 8 at one
+// vector per thread takes batches of 12, which keeps its unrolled batches
+// within the 128 VGPRs of a 1024-thread launch bound without spilling.
 constexpr int slots_in_flight(Layout l, int kc, int vpt)
 {
-    if (kc == kSmallTopK)
-        return 8 * vpt <= max_vecs(l, vpt) ? 8 : max_vecs(l, vpt) / vpt;
-    return (kc > 0 && kc * vpt <= max_vecs(l, vpt)) ? kc : max_vecs(l, vpt) / vpt;
+    const int want = kc < 0 ? -kc : kc;
+    if (kc == 0 && vpt == 1)
+        return max_vecs(l, vpt) < 12 ? max_vecs(l, vpt) : 12;
+    return (want > 0 && want * vpt <= max_vecs(l, vpt)) ? want : max_vecs(l, vpt) / vpt;
 }
 
 template <int VPT>
@@ -210,8 +217,8 @@ constexpr int max_team() { return VPT == 1 ? 1024 : VPT == 2 ? 512 : 256; }
 //   L      where slot rows come from (index map, token major, one row per token)
 //   W_BF16 weights are BF16 (else FP32)
 //   EPI    what follows the FP32 routed sum
-//   KC     top_k when known at compile time (0: read a.top_k; kSmallTopK:
-//          read a.top_k, which is at most 8)
+//   KC     top_k when known at compile time (0: read a.top_k; negative: read
+//          a.top_k, which is at most -KC)
 //   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
 template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
 __global__ void __launch_bounds__(max_team<VPT>())
@@ -265,7 +272,14 @@ finalize_kernel(const FinalizeArgs a)
         for (int e = 0; e < 8; ++e)
             acc[i][e] = 0.0f;
 
-    for (int k0 = 0; k0 < top_k; k0 += KB) {
+    // Batches are unrolled up to the largest top-k the entry points accept,
+    // with a uniform exit: a loop with a run-time trip count makes the
+    // compiler wait for every earlier load before each gather.
+    constexpr int kSlotsMax = KC > 0 ? KC : KC < 0 ? -KC : kMaxTopK;
+#pragma unroll
+    for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
+        if (KC <= 0 && k0 >= top_k)
+            break;
         // Uniform per-slot data first (scalar loads, one wait), then every
         // valid slot's row vectors, then the FMAs in ascending slot order.
         int64_t row_off[KB];   // elements
@@ -319,6 +333,11 @@ finalize_kernel(const FinalizeArgs a)
                         acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
             }
         }
+        // Every gather of this batch has been consumed.  Saying so keeps the
+        // compiler, which cannot pair each conditional load with its
+        // conditional use, from waiting before each gather of the next batch.
+        if constexpr (kSlotsMax > KB)
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     const __amdgpu_buffer_rsrc_t out_row =
@@ -506,30 +525,49 @@ constexpr bool vpt_reachable(int vpt)
     return false;
 }
 
-// Vectors per thread for hidden = 256 n: one for index-map rows up to
-// MF_INDEX_MAP_VPT1_MAX_HIDDEN, else the first of MF_VPT_ORDER whose
-// team of 32 n / VPT threads is a whole number of waves within the launch
-// bound; 0 if none (then one vector per thread with the last half wave idle).
-inline int pick_vpt(Layout l, int n)
+// Whether a team of 32 n / vpt threads is a whole number of waves within the
+// launch bound of that vpt.
+inline bool team_fits(int n, int vpt)
 {
+    const int team = 32 * n / vpt;
+    const int bound = vpt == 1 ? 1024 : vpt == 2 ? 512 : 256;
+    return (32 * n) % vpt == 0 && team % kWave == 0 && team >= kWave && team <= bound;
+}
+
+// Vectors per thread for hidden = 256 n: one for index-map rows up to
+// MF_INDEX_MAP_VPT1_MAX_HIDDEN, else the first of MF_VPT_ORDER whose team
+// fits; 0 if none (then one vector per thread with the last half wave idle).
+// On the index map, a run-time top-k below 8 (kc < 0) widens that by
+// 8 / -kc where the team still fits, so a thread keeps about as many row
+// vectors in flight as at top-k 8 while workgroups stay small enough for
+// high occupancy (2-8 % faster at top-k 2 and 4; token-major rows measured
+// faster without it).
+inline int pick_vpt(Layout l, int n, int kc)
+{
+    int base = 0;
     if (l == Layout::kIndexMap && 256 * n <= MF_INDEX_MAP_VPT1_MAX_HIDDEN && n % 2 == 0 &&
-        vpt_reachable(1))
-        return 1;
-    for (int vpt : {MF_VPT_ORDER}) {
-        const int team = 32 * n / vpt;
-        const int bound = vpt == 1 ? 1024 : vpt == 2 ? 512 : 256;
-        if ((32 * n) % vpt == 0 && team % kWave == 0 && team <= bound)
-            return vpt;
+        vpt_reachable(1)) {
+        base = 1;
+    } else {
+        for (int vpt : {MF_VPT_ORDER})
+            if (team_fits(n, vpt)) {
+                base = vpt;
+                break;
+            }
     }
-    return 0;
+    if (l == Layout::kIndexMap && kc < 0 && base > 0)
+        for (int vpt = std::min(8, base * 8 / -kc); vpt > base; vpt /= 2)
+            if (team_fits(n, vpt))
+                return vpt;
+    return base;
 }
 
 // Dynamic LDS to reserve per workgroup so that a CU holds
-// max(2, MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup) workgroups.
-// Beyond that, extra concurrent gathers do not raise bandwidth; they stretch
-// every token's lifetime and with it the tail of the launch (measured: 2-5 %
-// faster on every large workload than residency limited by registers).  The
-// kernels' own LDS use is 64 bytes.
+// ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup) workgroups,
+// clamped to 2..16.  Beyond that, extra concurrent gathers do not raise
+// bandwidth; they stretch every token's lifetime and with it the tail of
+// the launch (measured: 2-5 % faster on every large workload than residency
+// limited by registers).  The kernels' own LDS use is 64 bytes.
 inline size_t residency_lds(int hidden, int slots)
 {
 #if MF_INFLIGHT_KB_PER_CU > 0
@@ -551,7 +589,8 @@ inline size_t residency_lds(int hidden, int slots)
         lds_per_block[dev].store(blk, std::memory_order_relaxed);
     }
     const int64_t per_block = 2LL * hidden * slots;           // row bytes in flight
-    const int64_t blocks = std::max<int64_t>(2, (int64_t)MF_INFLIGHT_KB_PER_CU * 1024 / per_block);
+    const int64_t want = ((int64_t)MF_INFLIGHT_KB_PER_CU * 1024 + per_block - 1) / per_block;
+    const int64_t blocks = std::min<int64_t>(16, std::max<int64_t>(2, want));
     const int64_t lds = std::min<int64_t>(cu / blocks - 1024, blk);
     return lds > 0 ? (size_t)lds : 0;
 #else
@@ -564,32 +603,35 @@ inline size_t residency_lds(int hidden, int slots)
 template <Layout L, bool W_BF16, Epilogue EPI, int KC>
 hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
 {
+    if (a.top_k < 1 || a.top_k > kMaxTopK || (KC > 0 && a.top_k != KC) ||
+        (KC < 0 && a.top_k > -KC))
+        return hipErrorInvalidValue;
     const int n = a.hidden / 256;
     const int nv = 32 * n;
     const dim3 grid((unsigned)a.num_tokens);
-    const int vpt = pick_vpt(L, n);
+    const int vpt = pick_vpt(L, n, KC);
     // Slots actually in flight: with top-k read at run time the batch may be
     // larger than top-k, and the cap must follow the rows really fetched.
     const int slots = std::min(KC > 0 ? KC : a.top_k, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
     const size_t lds = residency_lds(a.hidden, slots);
     switch (vpt) {
     case 8:
-        if constexpr (vpt_reachable(8))
+        if constexpr (vpt_reachable(8) || KC < 0)
             hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid,
                                dim3(nv / 8), lds, s, a);
         break;
     case 4:
-        if constexpr (vpt_reachable(4))
+        if constexpr (vpt_reachable(4) || KC < 0)
             hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid,
                                dim3(nv / 4), lds, s, a);
         break;
     case 2:
-        if constexpr (vpt_reachable(2))
+        if constexpr (vpt_reachable(2) || KC < 0)
             hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid,
                                dim3(nv / 2), lds, s, a);
         break;
     case 1:
-        if constexpr (vpt_reachable(1))
+        if constexpr (vpt_reachable(1) || KC < 0)
             hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid,
                                dim3(nv), lds, s, a);
         break;
@@ -612,7 +654,11 @@ hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
     case 16:
         return launch_shape<L, W_BF16, EPI, 16>(a, s);
     default:
-        return a.top_k < 8 ? launch_shape<L, W_BF16, EPI, kSmallTopK>(a, s)
+        if (a.top_k <= 2)
+            return launch_shape<L, W_BF16, EPI, small_topk_kc(2)>(a, s);
+        if (a.top_k <= 4)
+            return launch_shape<L, W_BF16, EPI, small_topk_kc(4)>(a, s);
+        return a.top_k < 8 ? launch_shape<L, W_BF16, EPI, small_topk_kc(7)>(a, s)
                            : launch_shape<L, W_BF16, EPI, 0>(a, s);
     }
 }
