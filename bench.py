@@ -10,6 +10,7 @@ device copies of the row matrix and output (at least 1.5 GiB in total), so
 every step reads its rows from HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config prefill]
+    python bench.py --envelope        (the fused kernel over hidden x top-k)
 
 Prints one JSON line on stdout (diagnostics go to stderr): tokens/s over the
 timed region, the dominant kernel's achieved HBM bandwidth against the
@@ -73,6 +74,9 @@ def parse_args():
     p.add_argument("--graph", action="store_true",
                    help="capture the timed steps in one HIP graph and replay it (for "
                         "launch-bound small workloads)")
+    p.add_argument("--envelope", action="store_true",
+                   help="instead of one workload, time the fused kernel over a grid of "
+                        "hidden sizes and top-k on both layouts")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -391,6 +395,73 @@ def copy_ceiling(torch, mib: int = 1024, reps: int = 10) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+ENVELOPE_HIDDEN = (2048, 4096, 7168)
+ENVELOPE_TOPK = (1, 2, 4, 6, 8, 12, 16, 32)
+ENVELOPE_ROW_BYTES = 256 << 20      # gathered row bytes per launch (before rotation)
+
+
+def envelope(torch, mf, wl, steps: int, warmup: int) -> dict:
+    """Fused kernel time over hidden x top-k on both layouts: index map
+    (expert-grouped Zipf 1.1 map, FP32 weights, RMSNorm) and token major
+    (post-norm).  Inputs are seeded N(0,1) rows made on the device; the
+    token count gives about 256 MiB of gathered rows per launch, and steps
+    rotate over copies totalling at least 1.5 GiB, as in the main bench."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    results = []
+    for layout in ("index_map", "token_major"):
+        for H in ENVELOPE_HIDDEN:
+            for K in ENVELOPE_TOPK:
+                T = max(256, min(32768, ENVELOPE_ROW_BYTES // (K * H * 2)))
+                gen.manual_seed(1000 * H + K)
+                rng = np.random.Generator(np.random.PCG64(1000 * H + K))
+                w = torch.from_numpy(wl.softmax_rows(rng.standard_normal((T, K)) * 2.0)).to(dev)
+                nw = (torch.randn(H, generator=gen, device=dev) * 0.1).to(torch.bfloat16)
+                rows = torch.randn((T * K, H), generator=gen, device=dev).to(torch.bfloat16)
+                per_set = rows.numel() * 2 + T * H * 2
+                sets = max(2, math.ceil(ROTATE_MIN_BYTES / per_set))
+                rs = [rows] + [rows.clone() for _ in range(sets - 1)]
+                outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+                if layout == "index_map":
+                    idx = torch.from_numpy(wl.zipf_grouped_index_map(rng, T, K, 256, 1.1)).to(dev)
+                    nbytes = T * K * H * 2 + T * H * 2 + T * K * 8 + H * 2
+
+                    def step(i):
+                        mf.moe_finalize_rmsnorm(rs[i % sets], w, idx, nw, outs[i % sets],
+                                                eps=1e-6, gain_center=1.0,
+                                                weight_before_norm=False)
+                else:
+                    rs = [r.view(T, K, H) for r in rs]
+                    nbytes = T * K * H * 2 + T * H * 2 + T * K * 4 + H * 2
+
+                    def step(i):
+                        mf.beam_moe_finalize(rs[i % sets], w, outs[i % sets], 1.0, nw, 1e-6)
+                for i in range(warmup):
+                    step(i)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(steps):
+                    step(warmup + i)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / steps
+                gbps = nbytes / us / 1e3
+                results.append({"layout": layout, "hidden": H, "top_k": K, "tokens": T,
+                                "kernel_us": us, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS})
+                log(f"bench: envelope {layout} H={H} K={K} T={T}: {us:.2f} us, "
+                    f"{gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f} %)")
+                del rs, outs, rows
+                torch.cuda.empty_cache()
+    fr = sorted(r["frac"] for r in results)
+    return {"metric": "achieved HBM GB/s of the fused finalize over the hidden x top-k envelope",
+            "value": fr[len(fr) // 2] * PEAK_HBM_GBPS, "unit": "GB/s", "statistic": "median",
+            "min_frac": fr[0], "median_frac": fr[len(fr) // 2], "max_frac": fr[-1],
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True,
+            "data": "synthetic", "shapes": results}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -411,6 +482,10 @@ def main():
 
     import moe_expert_output_finalize_amd as mf
     import workloads as wl
+
+    if args.envelope:
+        print(json.dumps(envelope(torch, mf, wl, args.steps, args.warmup)), flush=True)
+        return
 
     log(f"bench: generating the {args.config} workload")
     if args.config == "beam5_residual":

@@ -18,9 +18,9 @@
 //    wave reads 1 KiB contiguous runs of each gathered row;
 //  - the token's indices and weights are uniform, so they live in SGPRs and
 //    validity is a scalar branch: invalid slots issue no memory traffic;
-//  - up to 32 (index map) or 16 (token major) row vectors per thread are in
-//    flight before the first FMA: all of a token's rows at top-k 8, and at
-//    top-k 16 on the index map; larger top-k in batches;
+//  - up to 16 row vectors per thread are in flight before the first FMA:
+//    all of a token's rows at top-k 8, and at top-k 16 with one vector per
+//    thread (index map up to hidden 4096); larger top-k in batches;
 //  - the FP32 sum, the sum of squares and the normalised values stay in
 //    VGPRs; the cross-lane sum uses DPP row operations, the cross-wave sum
 //    one LDS exchange and barrier;
@@ -53,12 +53,14 @@
 #define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
                                   // loads in flight total about this much per CU
 #endif
-// Row vectors in flight per thread.  Scattered index-map rows want every
-// slot in flight (top-k 16 at two vectors per thread: 14 % faster than two
-// batches of 8); a token-major token is one contiguous block, which is
-// faster fetched in halves (top-k 16: 10 % faster than all at once).
+// Row vectors in flight per thread.  16 (64 VGPRs) keeps two workgroups per
+// CU at two vectors per thread; 32 had let an index-map top-k 16 token have
+// all its rows in flight, but at hidden above 4096 the 150-160 VGPRs that
+// takes leave one workgroup per CU (hidden 5120-8192, top-k 12-16: 3-11 %
+// slower than batches of 8).  A token-major token is one contiguous block,
+// also faster fetched in halves (top-k 16: 10 % faster than all at once).
 #ifndef MF_MAX_VECS_INDEX_MAP
-#define MF_MAX_VECS_INDEX_MAP 32
+#define MF_MAX_VECS_INDEX_MAP 16
 #endif
 #ifndef MF_MAX_VECS_TOKEN_MAJOR
 #define MF_MAX_VECS_TOKEN_MAJOR 16
