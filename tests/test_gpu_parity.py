@@ -98,7 +98,12 @@ def test_beam_config(name):
 # ------------------------------------------------------- envelope sweeps ----
 
 SWEEP_H = [256, 768, 1280, 2048, 3840, 4096, 7168, 8192]
-SWEEP_K = [1, 3, 8, 16, 32]
+# One top-k per kernel variant: run-time top-k sized for 2 slots (1, 2), 4
+# slots (3, 4) and 8 slots (6, 7), compile-time 8 and 16, and run-time top-k
+# above 8 in one batch (9, 12) or several (24, 32).  With the hidden sizes
+# above this also covers one, two, four and eight vectors per thread and the
+# half-idle last wave of odd hidden / 256.
+SWEEP_K = [1, 2, 3, 4, 6, 7, 8, 9, 12, 16, 24, 32]
 
 
 @pytest.mark.parametrize("hidden", SWEEP_H)
