@@ -84,8 +84,15 @@ def _raise_on(name: str, rc: int) -> None:
         raise FinalizeError(name, rc, msg + (f": {extra}" if extra else ""))
 
 
-def _stream(stream, device) -> int | None:
+# The current stream's raw handle without building a Stream object (torch's
+# own kernel launchers use the same call); the public route costs ~2 us a call.
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: int) -> int | None:
     if stream is None:
+        if _current_raw_stream is not None:
+            return _current_raw_stream(device)
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -95,14 +102,17 @@ def _require(cond: bool, name: str, what: str) -> None:
         raise ValueError(f"{name}: {what}")
 
 
-def _check_device(name: str, *tensors) -> torch.device:
+def _check_device(name: str, *tensors) -> int:
+    """Index of the one GPU that holds every given tensor (None entries skipped)."""
     dev = None
     for t in tensors:
         if t is None:
             continue
-        _require(t.is_cuda, name, "tensors must be on a GPU")
-        dev = t.device if dev is None else dev
-        _require(t.device == dev, name, "tensors must be on one device")
+        d = t.get_device()
+        _require(d >= 0, name, "tensors must be on a GPU")
+        if dev is None:
+            dev = d
+        _require(d == dev, name, "tensors must be on one device")
     return dev
 
 
@@ -115,21 +125,22 @@ def _weights_dtype(name: str, w: torch.Tensor) -> int:
 
 
 def _index_map_args(name, gemm2_permuted, expert_weights, idx, output):
-    _require(gemm2_permuted.dim() == 2 and gemm2_permuted.dtype == torch.bfloat16, name,
+    gshape, ishape, oshape = gemm2_permuted.shape, idx.shape, output.shape
+    _require(len(gshape) == 2 and gemm2_permuted.dtype == torch.bfloat16, name,
              "gemm2_permuted must be a 2-D bfloat16 tensor")
-    _require(gemm2_permuted.stride(1) == 1 or gemm2_permuted.shape[1] <= 1, name,
+    gstride = gemm2_permuted.stride()
+    _require(gstride[1] == 1 or gshape[1] <= 1, name,
              "gemm2_permuted must have a unit-stride last dimension")
-    _require(idx.dim() == 2 and idx.dtype == torch.int32 and idx.is_contiguous(), name,
+    _require(len(ishape) == 2 and idx.dtype == torch.int32 and idx.is_contiguous(), name,
              "expanded_idx_to_permuted_idx must be a contiguous int32 [tokens, top_k] tensor")
-    _require(expert_weights.shape == idx.shape and expert_weights.is_contiguous(), name,
+    _require(expert_weights.shape == ishape and expert_weights.is_contiguous(), name,
              "expert_weights must be contiguous with the index map's shape")
-    _require(output.dim() == 2 and output.dtype == torch.bfloat16 and output.is_contiguous(),
+    _require(len(oshape) == 2 and output.dtype == torch.bfloat16 and output.is_contiguous(),
              name, "output must be a contiguous bfloat16 [tokens, hidden] tensor")
-    _require(output.shape[0] == idx.shape[0], name, "output and index map disagree on tokens")
-    _require(gemm2_permuted.shape[1] >= output.shape[1], name,
-             "gemm2_permuted is narrower than hidden")
-    row_stride = gemm2_permuted.stride(0) if gemm2_permuted.shape[0] > 1 else gemm2_permuted.shape[1]
-    return (gemm2_permuted.data_ptr(), gemm2_permuted.shape[0], row_stride,
+    _require(oshape[0] == ishape[0], name, "output and index map disagree on tokens")
+    _require(gshape[1] >= oshape[1], name, "gemm2_permuted is narrower than hidden")
+    row_stride = gstride[0] if gshape[0] > 1 else gshape[1]
+    return (gemm2_permuted.data_ptr(), gshape[0], row_stride,
             expert_weights.data_ptr(), _weights_dtype(name, expert_weights), idx.data_ptr())
 
 
