@@ -468,3 +468,39 @@ def test_runs_on_the_given_stream():
                                 gain_center=c.gain_center, weight_before_norm=False)
     s.synchronize()
     assert_within_ulp(host_bits(out), oracle_rmsnorm(c), 1, NORM_MIN_EXACT, "side stream")
+
+
+def test_host_threads_call_concurrently():
+    """The library keeps no shared mutable state beyond a per-device cache of
+    LDS limits: host threads launching on their own streams at the same time
+    get the results of serial calls."""
+    import threading
+    c = wl.tiny(num_tokens=300, num_rows=2400, invalid_frac=0.03)
+    d = IndexMapOnDevice(c)
+    want = gpu_rmsnorm(d)
+    outs, errors = [], []
+
+    def worker(seed):
+        try:
+            s = torch.cuda.Stream()
+            mine = [d.new_output() for _ in range(8)]
+            sync()
+            with torch.cuda.stream(s):
+                for o in mine:
+                    mf.moe_finalize_rmsnorm(d.gemm2, d.weights, d.idx, d.norm_weight, o,
+                                            eps=c.eps, gain_center=c.gain_center,
+                                            weight_before_norm=False)
+            s.synchronize()
+            outs.extend(mine)
+        except Exception as e:   # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert len(outs) == 32
+    for o in outs:
+        assert_bits_equal(host_bits(o), want, "threaded call")
