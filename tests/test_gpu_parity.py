@@ -504,3 +504,33 @@ def test_host_threads_call_concurrently():
     assert len(outs) == 32
     for o in outs:
         assert_bits_equal(host_bits(o), want, "threaded call")
+
+
+def test_output_offsets_beyond_4_gib_sampled():
+    """2.2 M tokens of hidden 1024 (4.5 GB of output, its second half past
+    2^32 bytes) gathering from 65536 shared rows, with 1.5 % of the indices
+    negative: a grid of millions of workgroups and 64-bit token and output
+    offsets.  Sampled tokens, spread over the whole
+    range and including the last, are compared with the oracle."""
+    T, H, K, R = 2_200_000, 1024, 2, 65536
+    assert T * H * 2 > 2 ** 32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    rows = torch.randn((R, H), generator=gen, device="cuda").to(torch.bfloat16)
+    idx = torch.randint(-R // 64, R, (T, K), generator=gen, device="cuda", dtype=torch.int32)
+    w = torch.softmax(torch.randn((T, K), generator=gen, device="cuda"), dim=1)
+    nw = (1.0 + 0.1 * torch.randn(H, generator=gen, device="cuda")).to(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    mf.moe_finalize_rmsnorm(rows, w, idx, nw, out, eps=1e-6, gain_center=0.0,
+                            weight_before_norm=True)
+    sync()
+    rng = np.random.Generator(np.random.PCG64(78))
+    pick = np.unique(np.concatenate([rng.integers(0, T, 2000), [0, T - 1, 2 ** 21 + 5]]))
+    pick_t = torch.from_numpy(pick).cuda()
+    got = host_bits(out[pick_t])
+    want = oracle.moe_finalize_rmsnorm(host_bits(rows), w[pick_t].cpu().numpy(),
+                                       idx[pick_t].cpu().numpy(), host_bits(nw), eps=1e-6,
+                                       gain_center=0.0, weight_before_norm=True)
+    assert_within_ulp(got, want, 1, NORM_MIN_EXACT, "sampled tokens past 4 GiB of output")
+    del out, rows
+    torch.cuda.empty_cache()
