@@ -534,3 +534,31 @@ def test_output_offsets_beyond_4_gib_sampled():
     assert_within_ulp(got, want, 1, NORM_MIN_EXACT, "sampled tokens past 4 GiB of output")
     del out, rows
     torch.cuda.empty_cache()
+
+
+def test_token_major_offsets_beyond_4_gib_sampled():
+    """Token-major rows of 300 000 tokens x top-k 8 x hidden 1024 (4.9 GB):
+    the rows of the later tokens start past 2^32 bytes.  Sampled tokens are
+    compared with the oracle on their own rows."""
+    C, K, H = 300_000, 8, 1024
+    assert C * K * H * 2 > 2 ** 32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(79)
+    e = torch.empty((C, K, H), dtype=torch.bfloat16, device="cuda")
+    for s in range(0, C, 50_000):        # in slices: no 10 GB FP32 temporary
+        e[s:s + 50_000] = torch.randn((min(50_000, C - s), K, H), generator=gen,
+                                      device="cuda").to(torch.bfloat16)
+    w = torch.softmax(torch.randn((C, K), generator=gen, device="cuda"), dim=1)
+    pw = (1.0 + 0.05 * torch.randn(H, generator=gen, device="cuda")).to(torch.bfloat16)
+    out = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
+    mf.beam_moe_finalize(e, w, out, 1.5, pw, 1e-6)
+    sync()
+    rng = np.random.Generator(np.random.PCG64(80))
+    pick = np.unique(np.concatenate([rng.integers(0, C, 1000), [0, C - 1]]))
+    pick_t = torch.from_numpy(pick).cuda()
+    got = host_bits(out[pick_t])
+    want = oracle.beam_moe_finalize(host_bits(e[pick_t]), w[pick_t].cpu().numpy(), len(pick),
+                                    1.5, host_bits(pw), 1e-6)
+    assert_within_ulp(got, want, 1, NORM_MIN_EXACT, "sampled token-major rows past 4 GiB")
+    del e, out
+    torch.cuda.empty_cache()
