@@ -334,16 +334,18 @@ def cpu_baseline(bench, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    worst, exact, within1, n = 0, 0, 0, 0
+    worst, exact, within1, n, nans = 0, 0, 0, 0, 0
     for want, got_t in zip(first, bench.gpu_outputs()):
         got = got_t.cpu().view(bench.torch.int16).numpy().view(np.uint16)
         d = bf16_ulp_distance(got, want)
         worst = max(worst, int(d.max()))
         exact += int((d == 0).sum())
         within1 += int((d <= 1).sum())
+        nans += int((((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)).sum())
         n += d.size
     agree = {"max_ulp": worst, "bit_exact_fraction": exact / max(n, 1),
-             "within_1_ulp_fraction": within1 / max(n, 1), "elements": n}
+             "within_1_ulp_fraction": within1 / max(n, 1), "elements": n,
+             "nan_outputs": nans, "unread_inputs": "NaN (padding columns, dead tokens)"}
     if getattr(bench, "agreement_note", None):
         agree["note"] = bench.agreement_note
     return {"value": reps * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -498,13 +500,18 @@ def main():
         return
 
     log(f"bench: generating the {args.config} workload")
+    # What is never read is filled with NaN (padding columns, rows and weights
+    # of tokens past the live count), so the oracle comparison at the end also
+    # shows that nothing leaks; it costs nothing, being never read.
     if args.config == "beam5_residual":
-        c = wl.beam5()
+        c = wl.beam5(poison_dead=True)
         bench = ResidualBench(c, torch, mf)
+    elif args.config in ("beam4", "beam5"):
+        c = wl.CONFIGS[args.config](poison_dead=True)
+        bench = TokenMajorBench(c, torch, mf)
     else:
-        c = wl.CONFIGS[args.config]()
-        bench = (IndexMapBench if isinstance(c, wl.IndexMapCase) else TokenMajorBench)(
-            c, torch, mf)
+        c = wl.CONFIGS[args.config](poison=True)
+        bench = IndexMapBench(c, torch, mf)
     log(f"bench: {bench.sets} rotating buffer sets, {bench.bytes} algorithmic bytes/step")
 
     for i in range(args.warmup):
