@@ -40,6 +40,37 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(so, name), f"{name} declared in the header but not exported"
 
 
+def declared_prototypes():
+    """name -> list of parameter declarations, from the header's MF_API lines."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"MF_API\s+[\w\s\*]+?\b(\w+)\s*\(([^;]*?)\)\s*;", src, flags=re.S):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip()]
+        protos[m.group(1)] = [] if params == ["void"] else params
+    return protos
+
+
+_CTYPE = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "float": ctypes.c_float,
+          "int": ctypes.c_int}
+
+
+def test_binding_argtypes_match_the_header():
+    """The Python binding declares every entry point with the header's
+    parameter count and, for scalars, the header's C type (pointers are
+    passed as void *)."""
+    protos = declared_prototypes()
+    assert len(protos) == len(declared_functions())
+    for name, params in protos.items():
+        argtypes = getattr(mf.lib, name).argtypes
+        assert argtypes is not None and len(argtypes) == len(params), name
+        for decl, ct in zip(params, argtypes):
+            if "*" in decl:
+                assert ct in (ctypes.c_void_p, ctypes.c_char_p), (name, decl)
+            else:
+                ctype = decl.replace("const", "").split()[0]
+                assert ct is _CTYPE[ctype], (name, decl, ct)
+
+
 def test_status_strings():
     for code in range(7):
         s = mf.lib.mf_status_string(code).decode()
