@@ -28,6 +28,12 @@
  *    validation error nothing is launched and the output is untouched.
  *  - A call with zero output rows validates its arguments, launches nothing
  *    and returns MF_OK.
+ *  - Every token count the entry points accept (up to INT32_MAX) is served:
+ *    the pages set no limit on the number of tokens [TPF Parameters: output
+ *    (num_tokens, 4096)].  A call whose grid would span more than 2^31
+ *    work-items (one workgroup of up to 1024 threads per token) runs as
+ *    several launches on `stream`, in token order; the split is invisible
+ *    to the caller.
  *  - The output must not overlap any input.  Calls on different streams may
  *    run concurrently when their outputs do not overlap.
  *  - Numerics: the routed sum is a chain of FP32 fused multiply-adds over
@@ -106,7 +112,8 @@ enum mf_dtype {
  * Errors: NULL pointer when num_tokens > 0 (gemm2_permuted may be NULL when
  * num_rows == 0: every index is then invalid) -> MF_ERR_NULL_POINTER;
  * hidden or top_k outside the envelope, num_tokens < 0 or > INT32_MAX, num_rows < 0,
- * row_stride < hidden -> MF_ERR_BAD_SHAPE; bad weights_dtype
+ * row_stride < hidden, or a row matrix (num_rows x row_stride) too large to
+ * address -> MF_ERR_BAD_SHAPE; bad weights_dtype
  * -> MF_ERR_BAD_DTYPE; misaligned pointer or row_stride % 8 != 0 ->
  * MF_ERR_MISALIGNED.
  */

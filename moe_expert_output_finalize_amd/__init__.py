@@ -4,7 +4,8 @@ Thin ctypes layer over ``libmoe_finalize.so`` (C ABI in
 ``include/moe_finalize.h``).  It only marshals torch tensors into pointers,
 sizes and the current HIP stream; every step of the computation runs in the
 library's HIP kernels.  There is no fallback: if the library is not built,
-importing this package raises.
+or was built from other sources than the ones beside it, importing this
+package raises.
 
 Entry points (same names as the C ABI):
   moe_finalize_rmsnorm  index-map finalize + per-token RMSNorm
@@ -20,10 +21,17 @@ Entry points (same names as the C ABI):
   beam_norm_residual_norm
                         the residual add and next norm on their own (second step
                         of the page's unfused strategy)
+
+The binding checks what the C ABI cannot see (dtype, device, contiguity and
+that the tensors' shapes agree) and hands every size to the library, which
+enforces the value ranges (top-k, hidden, live rows against capacity and
+weight rows, optional weights only with their norm) and returns a status
+that becomes a ``FinalizeError`` (a ``ValueError``).
 """
 from __future__ import annotations
 
 import ctypes
+import importlib.util
 import os
 
 import torch
@@ -48,11 +56,34 @@ class FinalizeError(ValueError):
         self.status = status
 
 
+def _build_module():
+    spec = importlib.util.spec_from_file_location("_mf_build", os.path.join(_PKG, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def check_built(lib_path: str = LIB_PATH) -> None:
+    """Raise ImportError unless `lib_path` exists and was built from the
+    sources now beside it (the digest its build recorded matches)."""
+    how = ("build it with `python moe_expert_output_finalize_amd/build.py` "
+           "(or __graft_entry__.build())")
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is not built; {how}")
+    b = _build_module()
+    try:
+        with open(b.digest_path(lib_path)) as f:
+            recorded = f.read().strip()
+    except OSError:
+        raise ImportError(f"{lib_path} has no record of its sources; rebuild: {how}") from None
+    root = os.path.dirname(os.path.dirname(os.path.abspath(lib_path)))
+    if recorded != b.source_digest(root):
+        raise ImportError(f"{lib_path} was built from other sources than the ones beside it "
+                          f"(stale or a variant build); rebuild: {how}")
+
+
 def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(
-            f"{LIB_PATH} is not built; build it with "
-            "`python moe_expert_output_finalize_amd/build.py` (or __graft_entry__.build())")
+    check_built()
     so = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     so.moe_finalize_rmsnorm.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, i64, i32, i32,
@@ -97,51 +128,93 @@ def _stream(stream, device: int) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _require(cond: bool, name: str, what: str) -> None:
-    if not cond:
-        raise ValueError(f"{name}: {what}")
+# ------------------------------------------------------------ checks -------
+#
+# These run on every call, so each tensor's attributes are read once and an
+# error message is only built for a failed check.
+
+def _fail(name: str, what: str):
+    raise ValueError(f"{name}: {what}")
 
 
-def _check_device(name: str, *tensors) -> int:
+def _t(name: str, what: str, t, dtype, ndim: int, contiguous: bool = True):
+    """Shape of `t` after checking its dtype, rank and layout (contiguous, or
+    unit stride along the last dimension only)."""
+    if t is None:
+        _fail(name, f"{what} is required")
+    shape = t.shape
+    if (t.dtype is not dtype or len(shape) != ndim or
+            not (t.is_contiguous() if contiguous else (shape[-1] <= 1 or t.stride(-1) == 1))):
+        layout = "contiguous" if contiguous else "unit-stride rows"
+        _fail(name, f"{what} must be a {ndim}-D {layout} {dtype} tensor, got {t.dtype} "
+                    f"{tuple(shape)} with strides {t.stride()}")
+    return shape
+
+
+def _device(name: str, *tensors) -> int:
     """Index of the one GPU that holds every given tensor (None entries skipped)."""
     dev = None
     for t in tensors:
         if t is None:
             continue
         d = t.get_device()
-        _require(d >= 0, name, "tensors must be on a GPU")
-        if dev is None:
-            dev = d
-        _require(d == dev, name, "tensors must be on one device")
+        if d < 0 or (dev is not None and d != dev):
+            _fail(name, "tensors must be on one GPU")
+        dev = d
     return dev
 
 
+def _vector(name: str, what: str, t, hidden: int) -> int | None:
+    """Pointer of an optional BF16 [hidden] weight (None stays None)."""
+    if t is None:
+        return None
+    if _t(name, what, t, torch.bfloat16, 1)[0] != hidden:
+        _fail(name, f"{what} must have {hidden} elements")
+    return t.data_ptr()
+
+
+def _row_stride(t, shape) -> int:
+    """Elements between the rows of a 2-D tensor with unit-stride rows."""
+    return t.stride(0) if shape[0] > 1 else shape[1]
+
+
 def _weights_dtype(name: str, w: torch.Tensor) -> int:
-    if w.dtype == torch.bfloat16:
-        return MF_DTYPE_BF16
-    if w.dtype == torch.float32:
+    d = w.dtype
+    if d is torch.float32:
         return MF_DTYPE_FP32
-    raise ValueError(f"{name}: expert_weights must be bfloat16 or float32")
+    if d is torch.bfloat16:
+        return MF_DTYPE_BF16
+    _fail(name, "expert_weights must be bfloat16 or float32")
 
 
-def _index_map_args(name, gemm2_permuted, expert_weights, idx, output):
-    gshape, ishape, oshape = gemm2_permuted.shape, idx.shape, output.shape
-    _require(len(gshape) == 2 and gemm2_permuted.dtype == torch.bfloat16, name,
-             "gemm2_permuted must be a 2-D bfloat16 tensor")
-    gstride = gemm2_permuted.stride()
-    _require(gstride[1] == 1 or gshape[1] <= 1, name,
-             "gemm2_permuted must have a unit-stride last dimension")
-    _require(len(ishape) == 2 and idx.dtype == torch.int32 and idx.is_contiguous(), name,
-             "expanded_idx_to_permuted_idx must be a contiguous int32 [tokens, top_k] tensor")
-    _require(expert_weights.shape == ishape and expert_weights.is_contiguous(), name,
-             "expert_weights must be contiguous with the index map's shape")
-    _require(len(oshape) == 2 and output.dtype == torch.bfloat16 and output.is_contiguous(),
-             name, "output must be a contiguous bfloat16 [tokens, hidden] tensor")
-    _require(oshape[0] == ishape[0], name, "output and index map disagree on tokens")
-    _require(gshape[1] >= oshape[1], name, "gemm2_permuted is narrower than hidden")
-    row_stride = gstride[0] if gshape[0] > 1 else gshape[1]
-    return (gemm2_permuted.data_ptr(), gshape[0], row_stride,
-            expert_weights.data_ptr(), _weights_dtype(name, expert_weights), idx.data_ptr())
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _eps(eps) -> tuple[float, int]:
+    """An optional epsilon as the C ABI's (value, present) pair."""
+    return (0.0, 0) if eps is None else (float(eps), 1)
+
+
+# ------------------------------------------------- index-map entry points --
+#
+# FlashInfer "flashinfer.comm.tp_moe_finalize_rmsnorm", Parameters:
+# gemm2_permuted BF16 [rows, >= hidden] with unit-stride rows; expert_weights
+# BF16 or FP32 [tokens, top_k] and expanded_idx_to_permuted_idx int32
+# [tokens, top_k], both contiguous; norm_weight BF16 [hidden]; output BF16
+# [tokens, hidden], contiguous.
+
+def _index_map(name, gemm2_permuted, expert_weights, idx, output):
+    T, K = _t(name, "expanded_idx_to_permuted_idx", idx, torch.int32, 2)
+    wdt = _weights_dtype(name, expert_weights)
+    if _t(name, "expert_weights", expert_weights, expert_weights.dtype, 2) != (T, K):
+        _fail(name, "expert_weights must have the index map's shape")
+    To, H = _t(name, "output", output, torch.bfloat16, 2)
+    gshape = _t(name, "gemm2_permuted", gemm2_permuted, torch.bfloat16, 2, contiguous=False)
+    if To != T or gshape[1] < H:
+        _fail(name, "output must be [tokens, hidden] and gemm2_permuted at least hidden wide")
+    return (gemm2_permuted.data_ptr(), gshape[0], _row_stride(gemm2_permuted, gshape),
+            expert_weights.data_ptr(), wdt, idx.data_ptr(), T, H, K)
 
 
 def moe_finalize_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
@@ -150,19 +223,18 @@ def moe_finalize_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch.Ten
                          weight_before_norm: bool, stream=None) -> None:
     """Index-map finalize fused with per-token RMSNorm, written into ``output``."""
     name = "moe_finalize_rmsnorm"
-    dev = _check_device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
-                        norm_weight, output)
-    g, rows, stride, w, wdt, idx = _index_map_args(name, gemm2_permuted, expert_weights,
-                                                    expanded_idx_to_permuted_idx, output)
-    _require(norm_weight.dim() == 1 and norm_weight.dtype == torch.bfloat16 and
-             norm_weight.is_contiguous() and norm_weight.shape[0] == output.shape[1], name,
-             "norm_weight must be a contiguous bfloat16 [hidden] tensor")
-    T, K = expanded_idx_to_permuted_idx.shape
-    rc = lib.moe_finalize_rmsnorm(g, rows, stride, w, wdt, idx, norm_weight.data_ptr(),
-                                  output.data_ptr(), T, output.shape[1], K, float(eps),
-                                  float(gain_center), int(bool(weight_before_norm)),
+    dev = _device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
+                  norm_weight, output)
+    g, rows, stride, w, wdt, idx, T, H, K = _index_map(
+        name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx, output)
+    nw = _vector(name, "norm_weight", norm_weight, H)
+    if nw is None:
+        _fail(name, "norm_weight is required")
+    rc = lib.moe_finalize_rmsnorm(g, rows, stride, w, wdt, idx, nw, output.data_ptr(), T, H, K,
+                                  float(eps), float(gain_center), int(bool(weight_before_norm)),
                                   _stream(stream, dev))
-    _raise_on(name, rc)
+    if rc:
+        _raise_on(name, rc)
 
 
 def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
@@ -170,14 +242,50 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
                  stream=None) -> None:
     """Index-map finalize without a norm: output = bf16(FP32 routed sum)."""
     name = "moe_finalize"
-    dev = _check_device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
-                        output)
-    g, rows, stride, w, wdt, idx = _index_map_args(name, gemm2_permuted, expert_weights,
-                                                    expanded_idx_to_permuted_idx, output)
-    T, K = expanded_idx_to_permuted_idx.shape
-    rc = lib.moe_finalize(g, rows, stride, w, wdt, idx, output.data_ptr(), T, output.shape[1],
-                          K, _stream(stream, dev))
-    _raise_on(name, rc)
+    dev = _device(name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx, output)
+    g, rows, stride, w, wdt, idx, T, H, K = _index_map(
+        name, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx, output)
+    rc = lib.moe_finalize(g, rows, stride, w, wdt, idx, output.data_ptr(), T, H, K,
+                          _stream(stream, dev))
+    if rc:
+        _raise_on(name, rc)
+
+
+def mf_rmsnorm(input: torch.Tensor, norm_weight: torch.Tensor, output: torch.Tensor, *,
+               eps: float, gain_center: float, weight_before_norm: bool, stream=None) -> None:
+    """Standalone per-token RMSNorm of BF16 rows, written into ``output``."""
+    name = "mf_rmsnorm"
+    dev = _device(name, input, norm_weight, output)
+    T, H = _t(name, "output", output, torch.bfloat16, 2)
+    ishape = _t(name, "input", input, torch.bfloat16, 2, contiguous=False)
+    if ishape[0] != T or ishape[1] < H:
+        _fail(name, "input must have output's rows and be at least as wide")
+    nw = _vector(name, "norm_weight", norm_weight, H)
+    if nw is None:
+        _fail(name, "norm_weight is required")
+    rc = lib.mf_rmsnorm(input.data_ptr(), _row_stride(input, ishape), nw, output.data_ptr(), T,
+                        H, float(eps), float(gain_center), int(bool(weight_before_norm)),
+                        _stream(stream, dev))
+    if rc:
+        _raise_on(name, rc)
+
+
+# ----------------------------------------------- token-major entry points --
+#
+# vLLM "vllm.models.beam.nvidia.moe_finalize", Parameters of
+# beam_moe_finalize: expert_outputs contiguous BF16 [capacity, top_k, hidden];
+# expert_weights contiguous FP32 with top_k columns and a row per token slot;
+# the per-token destination (and, for the residual variants, the residual)
+# contiguous BF16 [tokens, hidden]; optional BF16 norm weights [hidden], each
+# used only when its epsilon is given.
+
+def _token_major(name, expert_outputs, expert_weights, per_token, what):
+    capacity, top_k, hidden = _t(name, "expert_outputs", expert_outputs, torch.bfloat16, 3)
+    wshape = _t(name, "expert_weights", expert_weights, torch.float32, 2)
+    pshape = _t(name, what, per_token, torch.bfloat16, 2)
+    if wshape[1] != top_k or pshape[1] != hidden:
+        _fail(name, f"expert_weights must have top_k columns and {what} hidden columns")
+    return capacity, top_k, hidden, wshape[0], pshape[0]
 
 
 def beam_moe_finalize(expert_outputs: torch.Tensor, expert_weights: torch.Tensor,
@@ -186,79 +294,40 @@ def beam_moe_finalize(expert_outputs: torch.Tensor, expert_weights: torch.Tensor
                       stream=None) -> torch.Tensor:
     """Token-major finalize of output.shape[0] live rows; returns ``output``."""
     name = "beam_moe_finalize"
-    dev = _check_device(name, expert_outputs, expert_weights, output, post_weight)
-    _require(expert_outputs.dim() == 3 and expert_weights.dim() == 2 and output.dim() == 2,
-             name, "expected [capacity, top_k, hidden], [rows, top_k] and [live, hidden]")
-    capacity, top_k, hidden = expert_outputs.shape
-    _require(expert_outputs.dtype == torch.bfloat16 and output.dtype == torch.bfloat16, name,
-             "expert_outputs and output must be bfloat16")
-    _require(expert_weights.dtype == torch.float32, name, "expert_weights must be float32")
-    for t in (expert_outputs, expert_weights, output):
-        _require(t.is_contiguous(), name, "tensors must be contiguous")
-    _require(output.shape[1] == hidden and expert_weights.shape[1] == top_k, name,
-             "hidden / top_k mismatch")
-    if post_weight is not None:
-        _require(post_eps is not None, name, "post_weight needs post_eps")
-        _require(post_weight.shape == (hidden,) and post_weight.dtype == torch.bfloat16 and
-                 post_weight.is_contiguous(), name,
-                 "post_weight must be a contiguous bfloat16 [hidden] tensor")
-    rc = lib.beam_moe_finalize(
-        expert_outputs.data_ptr(), capacity, top_k, hidden, expert_weights.data_ptr(),
-        expert_weights.shape[0], output.data_ptr(), output.shape[0],
-        None if post_weight is None else post_weight.data_ptr(), float(routed_scale),
-        float(post_eps or 0.0), int(post_eps is not None), _stream(stream, dev))
-    _raise_on(name, rc)
+    dev = _device(name, expert_outputs, expert_weights, output, post_weight)
+    capacity, top_k, hidden, wrows, live = _token_major(name, expert_outputs, expert_weights,
+                                                        output, "output")
+    pw = _vector(name, "post_weight", post_weight, hidden)
+    eps, has_norm = _eps(post_eps)
+    rc = lib.beam_moe_finalize(expert_outputs.data_ptr(), capacity, top_k, hidden,
+                               expert_weights.data_ptr(), wrows, output.data_ptr(), live, pw,
+                               float(routed_scale), eps, has_norm, _stream(stream, dev))
+    if rc:
+        _raise_on(name, rc)
     return output
 
 
-def mf_rmsnorm(input: torch.Tensor, norm_weight: torch.Tensor, output: torch.Tensor, *,
-               eps: float, gain_center: float, weight_before_norm: bool, stream=None) -> None:
-    """Standalone per-token RMSNorm of BF16 rows, written into ``output``."""
-    name = "mf_rmsnorm"
-    dev = _check_device(name, input, norm_weight, output)
-    _require(input.dim() == 2 and input.dtype == torch.bfloat16 and
-             (input.stride(1) == 1 or input.shape[1] <= 1), name,
-             "input must be a 2-D bfloat16 tensor with a unit-stride last dimension")
-    _require(output.dim() == 2 and output.dtype == torch.bfloat16 and output.is_contiguous() and
-             output.shape[0] == input.shape[0] and input.shape[1] >= output.shape[1], name,
-             "output must be a contiguous bfloat16 [tokens, hidden] tensor")
-    _require(norm_weight.dim() == 1 and norm_weight.dtype == torch.bfloat16 and
-             norm_weight.is_contiguous() and norm_weight.shape[0] == output.shape[1], name,
-             "norm_weight must be a contiguous bfloat16 [hidden] tensor")
-    stride = input.stride(0) if input.shape[0] > 1 else input.shape[1]
-    rc = lib.mf_rmsnorm(input.data_ptr(), stride, norm_weight.data_ptr(), output.data_ptr(),
-                        output.shape[0], output.shape[1], float(eps), float(gain_center),
-                        int(bool(weight_before_norm)), _stream(stream, dev))
-    _raise_on(name, rc)
-
-
-def _opt_ptr(t):
-    return None if t is None else t.data_ptr()
-
-
-def _outputs(name, residual, next_eps, hidden_out, normalized_out):
-    """(hidden, normalized) destinations: the given tensors, or new ones."""
-    def ok(t):
-        return (t.shape == residual.shape and t.dtype == torch.bfloat16 and t.is_contiguous()
-                and t.device == residual.device)
+def _residual_outputs(name, residual, has_next, hidden_out, normalized_out):
+    """(hidden, normalized) destinations: the given tensors, or new ones
+    shaped like the residual."""
+    shape = residual.shape
     if hidden_out is None:
         hidden_out = torch.empty_like(residual)
-    _require(ok(hidden_out), name, "hidden_out must be a contiguous bfloat16 tensor like residual")
-    if next_eps is None:
+    elif _t(name, "hidden_out", hidden_out, torch.bfloat16, 2) != shape:
+        _fail(name, "hidden_out must have the residual's shape")
+    if not has_next:
         return hidden_out, None
     if normalized_out is None:
         normalized_out = torch.empty_like(residual)
-    _require(ok(normalized_out), name,
-             "normalized_out must be a contiguous bfloat16 tensor like residual")
+    elif _t(name, "normalized_out", normalized_out, torch.bfloat16, 2) != shape:
+        _fail(name, "normalized_out must have the residual's shape")
     return hidden_out, normalized_out
 
 
-def _check_norm_weight(name, w, eps, hidden, what):
-    if w is None:
-        return
-    _require(eps is not None, name, f"{what} needs its eps")
-    _require(w.shape == (hidden,) and w.dtype == torch.bfloat16 and w.is_contiguous(), name,
-             f"{what} must be a contiguous bfloat16 [hidden] tensor")
+def _scales(scales) -> tuple[float, float]:
+    """The scales pair (finalized branch, residual); absent means (1, 1)."""
+    sx, sr = (1.0, 1.0) if scales is None else scales
+    return float(sx), float(sr)
 
 
 def beam_moe_finalize_norm_residual_norm(
@@ -274,29 +343,22 @@ def beam_moe_finalize_norm_residual_norm(
     [capacity * top_k, hidden] rows viewed per token).  ``hidden_out`` and
     ``normalized_out`` may be given to write into existing tensors."""
     name = "beam_moe_finalize_norm_residual_norm"
-    dev = _check_device(name, expert_outputs, expert_weights, residual, post_weight,
-                        next_weight)
-    _require(expert_outputs.dim() == 3 and expert_weights.dim() == 2 and residual.dim() == 2,
-             name, "expected [capacity, top_k, hidden], [rows, top_k] and [tokens, hidden]")
-    capacity, top_k, hidden = expert_outputs.shape
-    _require(expert_outputs.dtype == torch.bfloat16 and residual.dtype == torch.bfloat16,
-             name, "expert_outputs and residual must be bfloat16")
-    _require(expert_weights.dtype == torch.float32, name, "expert_weights must be float32")
-    for t in (expert_outputs, expert_weights, residual):
-        _require(t.is_contiguous(), name, "tensors must be contiguous")
-    _require(residual.shape[1] == hidden and expert_weights.shape[1] == top_k, name,
-             "hidden / top_k mismatch")
-    _check_norm_weight(name, post_weight, post_eps, hidden, "post_weight")
-    _check_norm_weight(name, next_weight, next_eps, hidden, "next_weight")
-    out_h, out_n = _outputs(name, residual, next_eps, hidden_out, normalized_out)
-    sx, sr = scales if scales is not None else (1.0, 1.0)
+    dev = _device(name, expert_outputs, expert_weights, residual, post_weight, next_weight,
+                  hidden_out, normalized_out)
+    capacity, top_k, hidden, wrows, T = _token_major(name, expert_outputs, expert_weights,
+                                                     residual, "residual")
+    pw = _vector(name, "post_weight", post_weight, hidden)
+    nw = _vector(name, "next_weight", next_weight, hidden)
+    peps, has_post = _eps(post_eps)
+    neps, has_next = _eps(next_eps)
+    out_h, out_n = _residual_outputs(name, residual, has_next, hidden_out, normalized_out)
+    sx, sr = _scales(scales)
     rc = lib.beam_moe_finalize_norm_residual_norm(
-        expert_outputs.data_ptr(), capacity, top_k, hidden, expert_weights.data_ptr(),
-        expert_weights.shape[0], residual.data_ptr(), _opt_ptr(post_weight),
-        _opt_ptr(next_weight), out_h.data_ptr(), _opt_ptr(out_n), residual.shape[0],
-        float(routed_scale), float(post_eps or 0.0), float(next_eps or 0.0), float(sx),
-        float(sr), int(post_eps is not None), int(next_eps is not None), _stream(stream, dev))
-    _raise_on(name, rc)
+        expert_outputs.data_ptr(), capacity, top_k, hidden, expert_weights.data_ptr(), wrows,
+        residual.data_ptr(), pw, nw, out_h.data_ptr(), _ptr(out_n), T, float(routed_scale),
+        peps, neps, sx, sr, has_post, has_next, _stream(stream, dev))
+    if rc:
+        _raise_on(name, rc)
     return out_h, out_n
 
 
@@ -309,22 +371,20 @@ def beam_norm_residual_norm(x: torch.Tensor, residual: torch.Tensor,
     """(Post-norm) -> residual add -> next norm of BF16 rows ``x``; returns
     (hidden, normalized or None), optionally written into given tensors."""
     name = "beam_norm_residual_norm"
-    dev = _check_device(name, x, residual, post_weight, next_weight)
-    _require(x.dim() == 2 and residual.dim() == 2 and x.dtype == torch.bfloat16 and
-             residual.dtype == torch.bfloat16, name, "x and residual must be 2-D bfloat16")
-    _require(x.stride(1) == 1 or x.shape[1] <= 1, name, "x needs a unit-stride last dimension")
-    _require(residual.is_contiguous() and x.shape[0] == residual.shape[0] and
-             x.shape[1] >= residual.shape[1], name, "x / residual shape mismatch")
-    hidden = residual.shape[1]
-    _check_norm_weight(name, post_weight, post_eps, hidden, "post_weight")
-    _check_norm_weight(name, next_weight, next_eps, hidden, "next_weight")
-    out_h, out_n = _outputs(name, residual, next_eps, hidden_out, normalized_out)
-    sx, sr = scales if scales is not None else (1.0, 1.0)
-    stride = x.stride(0) if x.shape[0] > 1 else x.shape[1]
+    dev = _device(name, x, residual, post_weight, next_weight, hidden_out, normalized_out)
+    T, hidden = _t(name, "residual", residual, torch.bfloat16, 2)
+    xshape = _t(name, "x", x, torch.bfloat16, 2, contiguous=False)
+    if xshape[0] != T or xshape[1] < hidden:
+        _fail(name, "x must have the residual's rows and be at least as wide")
+    pw = _vector(name, "post_weight", post_weight, hidden)
+    nw = _vector(name, "next_weight", next_weight, hidden)
+    peps, has_post = _eps(post_eps)
+    neps, has_next = _eps(next_eps)
+    out_h, out_n = _residual_outputs(name, residual, has_next, hidden_out, normalized_out)
+    sx, sr = _scales(scales)
     rc = lib.beam_norm_residual_norm(
-        x.data_ptr(), stride, residual.data_ptr(), _opt_ptr(post_weight), _opt_ptr(next_weight),
-        out_h.data_ptr(), _opt_ptr(out_n), residual.shape[0], hidden, float(post_eps or 0.0),
-        float(next_eps or 0.0), float(sx), float(sr), int(post_eps is not None),
-        int(next_eps is not None), _stream(stream, dev))
-    _raise_on(name, rc)
+        x.data_ptr(), _row_stride(x, xshape), residual.data_ptr(), pw, nw, out_h.data_ptr(),
+        _ptr(out_n), T, hidden, peps, neps, sx, sr, has_post, has_next, _stream(stream, dev))
+    if rc:
+        _raise_on(name, rc)
     return out_h, out_n

@@ -1,9 +1,15 @@
 """Build libmoe_finalize.so (gfx950) in-tree with hipcc.
 
     python moe_expert_output_finalize_amd/build.py [-o OUT] [-D MACRO=VALUE ...]
+
+Beside the library it writes ``<library>.sources``: a digest of every source
+and header the library is built from, which the Python binding compares with
+the tree it is imported from, so a library older than its sources is refused
+instead of being tested or timed.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -11,8 +17,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_finalize.so")
-SOURCES = ["capi.hip", "finalize_kernels.hip"]
+SOURCES = ["capi.cpp", "finalize_kernels.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -29,14 +36,46 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+PROBES_LIB = os.path.join(PKG, "libmf_probes.so")
+PROBES_SOURCE = "bench_probes.hip"
+
+
+def source_files(root: str = ROOT) -> list[str]:
+    """Every file the library is compiled from, in a fixed order."""
+    csrc = os.path.join(root, "moe_expert_output_finalize_amd", "csrc")
+    inc = os.path.join(root, "include")
+    files = [os.path.join(csrc, f) for f in SOURCES]
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith(".hpp")]
+    files += [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+    return files
+
+
+def source_digest(root: str = ROOT, defines: list[str] | None = None) -> str:
+    """SHA-256 over the names and contents of the library's sources, the
+    compiler flags and any extra definitions."""
+    h = hashlib.sha256()
+    h.update(" ".join(HIPCC_FLAGS + sorted(defines or [])).encode())
+    for path in source_files(root):
+        h.update(os.path.relpath(path, root).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def digest_path(lib: str) -> str:
+    return lib + ".sources"
+
+
 def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile the HIP sources into `out` (always recompiles)."""
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    """Compile the HIP sources into `out` (always recompiles) and record the
+    digest of what it was built from."""
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC]
     cmd += [f"-D{d}" for d in (defines or [])]
     tmp = out + f".tmp{os.getpid()}"
     cmd += ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
+    digest = source_digest(ROOT, defines)
     p = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag; drop that note
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -46,6 +85,21 @@ def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = Fals
     if msg.strip() and verbose:
         print(msg)
     os.replace(tmp, out)
+    with open(digest_path(out) + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(digest_path(out) + ".tmp", digest_path(out))
+    return out
+
+
+def build_probes(out: str = PROBES_LIB) -> str:
+    """Compile the benchmark's memory probes (csrc/bench_probes.hip) into
+    their own library, which the finalize ABI does not include."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, os.path.join(CSRC, PROBES_SOURCE)]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({p.returncode}):\n{p.stdout}{p.stderr}")
+    os.replace(tmp, out)
     return out
 
 
@@ -54,6 +108,6 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser(description="build libmoe_finalize.so for gfx950")
     ap.add_argument("-o", "--out", default=LIB)
     ap.add_argument("-D", dest="defines", action="append", default=[],
-                    help="extra preprocessor definition, e.g. -D MF_MAX_VECS=8")
+                    help="extra preprocessor definition, e.g. -D MF_MAX_VECS_INDEX_MAP=8")
     ns = ap.parse_args()
     print(build(out=ns.out, defines=ns.defines, verbose=True))

@@ -1,9 +1,10 @@
-// Internal interface between the C ABI (capi.hip) and the gfx950 kernels
-// (finalize_kernels.hip).  Not installed; the public interface is
-// include/moe_finalize.h.
+// Internal interface between the C ABI (capi.cpp) and the gfx950 kernels
+// (finalize_kernels.hip).  Plain C++ with no HIP types, so that the C ABI's
+// host code also builds with an ordinary host compiler (the sanitizer build
+// of the tests links it against a recording stand-in for launch_finalize).
+// Not installed; the public interface is include/moe_finalize.h.
 #pragma once
 
-#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mf {
@@ -27,7 +28,9 @@ enum class Epilogue : int {
                          // out2 = bf16(h * inv_rms(h) * next_weight) when has_next
 };
 
-// Arguments of one launch; validated by the caller.
+// Arguments of one call; validated by the caller.  Token t of the call
+// reads and writes the rows of token t; a launch covers the tokens
+// [token_base, token_base + gridDim.x).
 struct FinalizeArgs {
     const uint16_t *rows;     // BF16 row matrix (see Layout)
     int64_t row_stride;       // elements between rows (index map, direct)
@@ -37,7 +40,8 @@ struct FinalizeArgs {
     bool weights_bf16;
     const uint16_t *gain;     // BF16 [H]: norm_weight / post_weight (nullable for kBeamNorm)
     uint16_t *out;            // BF16 [T, H]
-    int32_t num_tokens;
+    int64_t num_tokens;       // tokens of the whole call
+    int64_t token_base;       // first token of this launch (set by the launcher)
     int32_t hidden;
     int32_t top_k;
     float eps;
@@ -52,11 +56,15 @@ struct FinalizeArgs {
     bool has_post, has_next;
 };
 
-// Enqueue the finalize on `stream`; returns the launch status.  Supported
-// pairs: index map with kRound / kRmsNorm / kRmsNormWeightFirst; token major
-// with kBeam / kBeamNorm / kResidualNorm; direct with kRmsNorm /
-// kRmsNormWeightFirst / kResidualNorm (routed_scale 1).
-hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi,
-                           hipStream_t stream);
+// Enqueue the finalize of all num_tokens tokens on `stream` (a hipStream_t),
+// in as many launches as the grid limit requires.  Returns 0 or the HIP error
+// code of the first failed launch.  Supported pairs: index map with kRound /
+// kRmsNorm / kRmsNormWeightFirst; token major with kBeam / kBeamNorm /
+// kResidualNorm; direct with kRmsNorm / kRmsNormWeightFirst / kResidualNorm
+// (routed_scale 1).
+int launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, void *stream);
+
+// Text of a code returned by launch_finalize (never NULL).
+const char *launch_error_string(int code);
 
 }  // namespace mf

@@ -1,0 +1,167 @@
+// Memory-system probes for the benchmark: plain streaming kernels whose
+// bandwidth bounds what a gather-reduce with the same traffic can reach on
+// this GPU.  Built into libmf_probes.so beside the finalize library; not part
+// of the finalize C ABI and declared in no public header.
+//
+//   mf_probe_read    read n16 16-byte vectors, write nothing (one flag word
+//                    only if the data hits an impossible value)
+//   mf_probe_write   write n16 16-byte vectors
+//   mf_probe_mixed   read `ratio` vectors from `ratio` equal slices of the
+//                    input for every vector written: the read:write mix of
+//                    the finalize (8:1 at top-k 8), all of it coalesced
+// (reads non-temporal, as the finalize's gathers; writes through a buffer
+// resource with a chosen cache policy, as the finalize's stores).
+//
+// Each thread moves 16-byte vectors in a grid-stride loop; `blocks` and
+// `threads` set the launch so the caller can take the best of several.
+// The arithmetic is integer adds and XORs, negligible against the traffic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void probe_read(const u32x4 *__restrict__ in, int64_t n16, uint32_t *flag)
+{
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(in + i);
+        const u32x4 b = __builtin_nontemporal_load(in + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(in + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(in + i + 3 * stride);
+        acc ^= a + b + c + d;
+    }
+    for (; i < n16; i += stride)
+        acc ^= __builtin_nontemporal_load(in + i);
+    if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x94D049BBu &&
+        acc.w == 0x2545F491u)
+        flag[0] = 1u + threadIdx.x;   // never in practice; keeps the loads alive
+}
+
+// Buffer resource over `bytes` bytes for raw 16-byte stores (gfx9 word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_resource(void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
+}
+
+// Stores take cache-policy operand POL (bit 0 sc0, bit 1 nt, bit 4 sc1), as
+// the finalize kernels' own output stores do.
+template <int POL>
+__global__ void probe_write(u32x4 *__restrict__ out, int64_t n16, uint32_t seed)
+{
+    const __amdgpu_buffer_rsrc_t r = out_resource(out, (uint32_t)(n16 * 16));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const uint32_t v = seed ^ (uint32_t)i;
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){v, v + 1u, v + 2u, v + 3u}, r,
+                                               (uint32_t)(i * 16), 0, POL);
+    }
+}
+
+template <int R, int POL>
+__global__ void probe_mixed(const u32x4 *__restrict__ in, u32x4 *__restrict__ out,
+                            int64_t n16_out)
+{
+    const __amdgpu_buffer_rsrc_t r = out_resource(out, (uint32_t)(n16_out * 16));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16_out; i += stride) {
+        u32x4 v[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            v[k] = __builtin_nontemporal_load(in + k * n16_out + i);
+        u32x4 s = v[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k)
+            s += v[k];
+        __builtin_amdgcn_raw_buffer_store_b128(s, r, (uint32_t)(i * 16), 0, POL);
+    }
+}
+
+template <int POL>
+hipError_t launch_write(void *out, int64_t n16, dim3 g, dim3 b, hipStream_t s)
+{
+    hipLaunchKernelGGL(probe_write<POL>, g, b, 0, s, (u32x4 *)out, n16, 0x5bd1e995u);
+    return hipGetLastError();
+}
+
+template <int R, int POL>
+hipError_t launch_mixed(const void *in, void *out, int64_t n16_out, dim3 g, dim3 b,
+                        hipStream_t s)
+{
+    hipLaunchKernelGGL((probe_mixed<R, POL>), g, b, 0, s, (const u32x4 *)in, (u32x4 *)out,
+                       n16_out);
+    return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_mixed_pol(int policy, const void *in, void *out, int64_t n16_out, dim3 g,
+                            dim3 b, hipStream_t s)
+{
+    switch (policy) {
+    case 0: return launch_mixed<R, 0>(in, out, n16_out, g, b, s);
+    case 2: return launch_mixed<R, 2>(in, out, n16_out, g, b, s);
+    case 16: return launch_mixed<R, 16>(in, out, n16_out, g, b, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Every probe returns 0 or the HIP error of its launch; all pointers are
+// device pointers of at least the stated size, 16-byte aligned.
+
+__attribute__((visibility("default"))) int mf_probe_read(const void *in, int64_t n16,
+                                                          void *flag, int blocks, int threads,
+                                                          void *stream)
+{
+    if (!in || !flag || n16 <= 0 || blocks <= 0 || threads <= 0 || threads > 1024)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(threads), 0, (hipStream_t)stream,
+                       (const u32x4 *)in, n16, (uint32_t *)flag);
+    return (int)hipGetLastError();
+}
+
+// Stores of the write and mixed probes use cache policy `policy`: 0, 2 (nt)
+// or 16 (sc1); their output is below 4 GiB (one buffer resource spans it).
+__attribute__((visibility("default"))) int mf_probe_write(void *out, int64_t n16, int policy,
+                                                           int blocks, int threads,
+                                                           void *stream)
+{
+    if (!out || n16 <= 0 || n16 >= (int64_t(1) << 28) || blocks <= 0 || threads <= 0 ||
+        threads > 1024)
+        return (int)hipErrorInvalidValue;
+    const dim3 g(blocks), b(threads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (policy) {
+    case 0: return (int)launch_write<0>(out, n16, g, b, s);
+    case 2: return (int)launch_write<2>(out, n16, g, b, s);
+    case 16: return (int)launch_write<16>(out, n16, g, b, s);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+// in: ratio * n16_out vectors; out: n16_out vectors.  ratio 4, 8 or 16.
+__attribute__((visibility("default"))) int mf_probe_mixed(const void *in, void *out,
+                                                           int64_t n16_out, int ratio,
+                                                           int policy, int blocks, int threads,
+                                                           void *stream)
+{
+    if (!in || !out || n16_out <= 0 || n16_out >= (int64_t(1) << 28) || blocks <= 0 ||
+        threads <= 0 || threads > 1024)
+        return (int)hipErrorInvalidValue;
+    const dim3 g(blocks), b(threads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (ratio) {
+    case 4: return (int)launch_mixed_pol<4>(policy, in, out, n16_out, g, b, s);
+    case 8: return (int)launch_mixed_pol<8>(policy, in, out, n16_out, g, b, s);
+    case 16: return (int)launch_mixed_pol<16>(policy, in, out, n16_out, g, b, s);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // extern "C"

@@ -1,7 +1,9 @@
-// C ABI of libmoe_finalize.so: argument validation and launch.
+// C ABI of libmoe_finalize.so: argument validation, then mf::launch_finalize.
 //
-// Every check runs on the host before any HIP call, so a rejected call has
-// no side effect.  The checks are the C form of the parameter contracts on
+// Plain C++ with no HIP types: every check runs on the host before any HIP
+// call, so a rejected call has no side effect, and the tests can build this
+// file with an ordinary host compiler under AddressSanitizer and
+// UndefinedBehaviorSanitizer against a recording stand-in for the launcher.  The checks are the C form of the parameter contracts on
 // the FlashInfer page "flashinfer.comm.tp_moe_finalize_rmsnorm" (Parameters:
 // shapes, dtypes, unit-stride rows with a row stride that is a multiple of 8
 // elements, 16-byte alignment) and of the argument
@@ -12,11 +14,10 @@
 // The FlashInfer page specialises its finalize+RMSNorm to hidden 4096 and
 // top-k 8; here every entry point accepts the wider envelope of the vLLM
 // checks, 4096 / 8 included.
-#include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 
-#include "launch.hpp"
+#include "args.hpp"
 #include "moe_finalize.h"
 
 namespace {
@@ -29,10 +30,10 @@ bool hidden_in_envelope(int32_t hidden) { return hidden >= 256 && hidden <= 8192
 
 int launch(const mf::FinalizeArgs &a, mf::Layout layout, mf::Epilogue epi, void *stream)
 {
-    const hipError_t err = mf::launch_finalize(a, layout, epi, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) {
+    const int err = mf::launch_finalize(a, layout, epi, stream);
+    if (err != 0) {
         snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s (%d)",
-                 hipGetErrorString(err), static_cast<int>(err));
+                 mf::launch_error_string(err), err);
         return MF_ERR_LAUNCH_FAILED;
     }
     g_last_error[0] = '\0';
@@ -48,7 +49,8 @@ int check_index_map(const void *gemm2_permuted, int64_t num_rows, int64_t row_st
 {
     if (num_tokens < 0 || num_tokens > INT32_MAX || num_rows < 0)
         return MF_ERR_BAD_SHAPE;
-    if (row_stride < hidden)
+    // The row matrix must be addressable: row_stride * num_rows elements.
+    if (row_stride < hidden || (num_rows > 0 && row_stride > INT64_MAX / 2 / num_rows))
         return MF_ERR_BAD_SHAPE;
     if (weights_dtype != MF_DTYPE_BF16 && weights_dtype != MF_DTYPE_FP32)
         return MF_ERR_BAD_DTYPE;
@@ -69,7 +71,7 @@ int check_index_map(const void *gemm2_permuted, int64_t num_rows, int64_t row_st
     a.weights = expert_weights;
     a.weights_bf16 = weights_dtype == MF_DTYPE_BF16;
     a.out = static_cast<uint16_t *>(output);
-    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.num_tokens = num_tokens;
     a.hidden = hidden;
     a.top_k = top_k;
     return MF_OK;
@@ -147,13 +149,13 @@ int beam_moe_finalize(const void *expert_outputs, int64_t capacity, int32_t top_
     mf::FinalizeArgs a{};
     a.rows = static_cast<const uint16_t *>(expert_outputs);
     a.row_stride = hidden;
-    a.num_rows = capacity * top_k;
+    a.num_rows = capacity;   // unused: token-major slots are never masked
     a.idx = nullptr;
     a.weights = expert_weights;
     a.weights_bf16 = false;
     a.gain = static_cast<const uint16_t *>(post_weight);
     a.out = static_cast<uint16_t *>(output);
-    a.num_tokens = static_cast<int32_t>(live_tokens);
+    a.num_tokens = live_tokens;
     a.hidden = hidden;
     a.top_k = top_k;
     a.eps = post_eps;
@@ -167,7 +169,7 @@ int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_weight, v
                int32_t weight_before_norm, void *stream)
 {
     if (!hidden_in_envelope(hidden) || num_tokens < 0 || num_tokens > INT32_MAX ||
-        row_stride < hidden)
+        row_stride < hidden || (num_tokens > 0 && row_stride > INT64_MAX / 2 / num_tokens))
         return MF_ERR_BAD_SHAPE;
     if (row_stride % 8 != 0)
         return MF_ERR_MISALIGNED;
@@ -183,7 +185,7 @@ int mf_rmsnorm(const void *input, int64_t row_stride, const void *norm_weight, v
     a.num_rows = num_tokens;
     a.gain = static_cast<const uint16_t *>(norm_weight);
     a.out = static_cast<uint16_t *>(output);
-    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.num_tokens = num_tokens;
     a.hidden = hidden;
     a.top_k = 1;
     a.eps = eps;
@@ -219,11 +221,11 @@ int beam_moe_finalize_norm_residual_norm(
     mf::FinalizeArgs a{};
     a.rows = static_cast<const uint16_t *>(expert_outputs);
     a.row_stride = hidden;
-    a.num_rows = capacity * top_k;
+    a.num_rows = capacity;   // unused: token-major slots are never masked
     a.weights = expert_weights;
     a.gain = static_cast<const uint16_t *>(post_weight);
     a.out = static_cast<uint16_t *>(hidden_out);
-    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.num_tokens = num_tokens;
     a.hidden = hidden;
     a.top_k = top_k;
     a.eps = post_eps;
@@ -246,7 +248,7 @@ int beam_norm_residual_norm(const void *x, int64_t row_stride, const void *resid
                             int32_t has_post_norm, int32_t has_next_norm, void *stream)
 {
     if (!hidden_in_envelope(hidden) || num_tokens < 0 || num_tokens > INT32_MAX ||
-        row_stride < hidden)
+        row_stride < hidden || (num_tokens > 0 && row_stride > INT64_MAX / 2 / num_tokens))
         return MF_ERR_BAD_SHAPE;
     if (row_stride % 8 != 0)
         return MF_ERR_MISALIGNED;
@@ -265,7 +267,7 @@ int beam_norm_residual_norm(const void *x, int64_t row_stride, const void *resid
     a.num_rows = num_tokens;
     a.gain = static_cast<const uint16_t *>(post_weight);
     a.out = static_cast<uint16_t *>(hidden_out);
-    a.num_tokens = static_cast<int32_t>(num_tokens);
+    a.num_tokens = num_tokens;
     a.hidden = hidden;
     a.top_k = 1;
     a.eps = post_eps;

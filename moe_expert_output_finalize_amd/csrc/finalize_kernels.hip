@@ -37,7 +37,8 @@
 #include <algorithm>
 #include <atomic>
 
-#include "launch.hpp"
+#include "args.hpp"
+#include "plan.hpp"
 
 #ifndef MF_NONTEMPORAL_ROWS
 #define MF_NONTEMPORAL_ROWS 1   // gathered rows are read exactly once
@@ -49,32 +50,10 @@
 #ifndef MF_STORE_POLICY
 #define MF_STORE_POLICY 16
 #endif
-#ifndef MF_INFLIGHT_KB_PER_CU
-#define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
-                                  // loads in flight total about this much per CU
-#endif
-// Row vectors in flight per thread.  16 (64 VGPRs) keeps two workgroups per
-// CU at two vectors per thread; 32 had let an index-map top-k 16 token have
-// all its rows in flight, but at hidden above 4096 the 150-160 VGPRs that
-// takes leave one workgroup per CU (hidden 5120-8192, top-k 12-16: 3-11 %
-// slower than batches of 8).  A token-major token is one contiguous block,
-// also faster fetched in halves (top-k 16: 10 % faster than all at once).
-#ifndef MF_MAX_VECS_INDEX_MAP
-#define MF_MAX_VECS_INDEX_MAP 16
-#endif
-#ifndef MF_MAX_VECS_TOKEN_MAJOR
-#define MF_MAX_VECS_TOKEN_MAJOR 16
-#endif
-#ifndef MF_VPT_ORDER
-#define MF_VPT_ORDER 2, 1, 4, 8 // preferred vectors per thread, first that fits
-#endif
-// Index-map rows up to this hidden size take one vector per thread instead
-// (teams of up to 512 threads): 1 % faster at 8192 tokens and hidden 4096,
-// 5 % at 256 tokens, 3 % at hidden 2048 / top-k 16; at hidden 7168 the
-// 896-thread teams are 5 % slower, and token-major tokens prefer two
-// vectors per thread at every size measured.  0 disables the override.
-#ifndef MF_INDEX_MAP_VPT1_MAX_HIDDEN
-#define MF_INDEX_MAP_VPT1_MAX_HIDDEN 4096
+// Cache-policy operand of row loads through buffer resources (the streaming
+// path): nt, as the global loads of the batch path.
+#ifndef MF_ROW_LOAD_POLICY
+#define MF_ROW_LOAD_POLICY 2
 #endif
 
 namespace mf {
@@ -84,11 +63,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
-constexpr int kMaxTopK = 32;   // the entry points reject larger top-k
 // s_waitcnt operand on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kMaxWaves = 16;
+// The kernel's own LDS: block_sum's two banks of per-wave partial sums.
+constexpr int kStaticLds = 2 * kMaxWaves * sizeof(float);
 
 // ------------------------------------------------------------ BF16 -------
 
@@ -182,52 +160,45 @@ __device__ __forceinline__ float block_sum(float v, int bank = 0)
     return s;
 }
 
+
+// Value of lane `l` (a constant) of v, as a wave-uniform scalar.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_value(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // ------------------------------------------------------------ kernel -----
 
-// Row vectors one thread keeps in flight.  One vector per thread means teams
-// of up to 1024 threads, whose launch bound leaves 128 VGPRs per thread: at
-// most 16 vectors (64 VGPRs) there.
-constexpr int max_vecs(Layout l, int vpt)
-{
-    const int m = l == Layout::kIndexMap ? MF_MAX_VECS_INDEX_MAP : MF_MAX_VECS_TOKEN_MAJOR;
-    return vpt == 1 && m > 16 ? 16 : m;
-}
-
-// Slot-count template argument for a top-k read at run time:
-//   KC > 0   top-k is KC;
-//   KC == 0  any top-k, in batches of max_vecs / VPT slots;
-//   KC < 0   top-k at most -KC, registers sized for -KC slots, so a small
-//            top-k keeps a small register footprint and high occupancy.
-constexpr int small_topk_kc(int top_k) { return top_k <= 2 ? -2 : top_k <= 4 ? -4 : -8; }
-
-// Slots whose rows one workgroup has in flight at once: all of them when
-// they fit, else batches of max_vecs / VPT; a run-time top-k above 8 at one
-// vector per thread takes batches of 12, which keeps its unrolled batches
-// within the 128 VGPRs of a 1024-thread launch bound without spilling.
-constexpr int slots_in_flight(Layout l, int kc, int vpt)
-{
-    const int want = kc < 0 ? -kc : kc;
-    if (kc == 0 && vpt == 1)
-        return max_vecs(l, vpt) < 12 ? max_vecs(l, vpt) : 12;
-    return (want > 0 && want * vpt <= max_vecs(l, vpt)) ? want : max_vecs(l, vpt) / vpt;
-}
-
-template <int VPT>
-constexpr int max_team() { return VPT == 1 ? 1024 : VPT == 2 ? 512 : 256; }
-
-// One workgroup finalizes token blockIdx.x.
+// One workgroup finalizes token a.token_base + blockIdx.x.
 //   L      where slot rows come from (index map, token major, one row per token)
 //   W_BF16 weights are BF16 (else FP32)
 //   EPI    what follows the FP32 routed sum
-//   KC     top_k when known at compile time (0: read a.top_k; negative: read
-//          a.top_k, which is at most -KC)
+//   KC     top_k when known at compile time (> 0), else minus the largest
+//          top-k the kernel serves (a.top_k is read at run time)
 //   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
+//
+// Slots whose rows all fit in flight (slots_in_flight) arrive as one batch:
+// every valid slot's row vectors are issued, then the FMAs run.  More slots
+// than that stream through a rolling window of W slots: the rows of slot
+// s + W are issued as soon as slot s has been reduced, so a token's loads
+// never drain between groups of slots.  The window's code is straight-line:
+// its loads go through buffer resources, and an invalid slot, or one past a
+// run-time top-k, gets an empty resource whose loads return zeros without
+// touching memory, and weight 0.  Every load is then unconditional, the
+// compiler waits for exactly the slot being reduced, and a scheduling
+// barrier per slot keeps each slot's loads W slots ahead of its FMAs instead
+// of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
+// starts at +0 never becomes -0.
 template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
-__global__ void __launch_bounds__(max_team<VPT>())
+__global__ void __launch_bounds__(max_team(VPT))
 finalize_kernel(const FinalizeArgs a)
 {
-    constexpr int KB = slots_in_flight(L, KC, VPT);
-    static_assert(KB >= 1 && (KC <= 0 || KC % KB == 0), "slot batch must divide top_k");
+    constexpr bool kIdx = L == Layout::kIndexMap;
+    constexpr int KB = slots_in_flight(kIdx, KC, VPT);
+    constexpr bool kRoll = rolling(kIdx, KC, VPT);
+    constexpr int kSlotsMax = KC > 0 ? KC : -KC;
+    static_assert(KB >= 1 && (kRoll || KC <= 0 || KC % KB == 0), "batches divide top-k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
     constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
@@ -236,7 +207,7 @@ finalize_kernel(const FinalizeArgs a)
     const int team = blockDim.x;
     const int lane = threadIdx.x;
     const int nv = a.hidden >> 3;
-    const int64_t t = blockIdx.x;
+    const int64_t t = a.token_base + blockIdx.x;
     const int64_t tk = t * top_k;
 
     // The norm weight is shared by every token and stays cache resident;
@@ -267,79 +238,155 @@ finalize_kernel(const FinalizeArgs a)
         }
     }
 
+    // A direct row starts from -0, so that fma(1, x, -0) == x for every x,
+    // -0 included; a routed sum starts from +0.
+    constexpr float kAcc0 = L == Layout::kDirect ? -0.0f : 0.0f;
     float acc[VPT][8];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            acc[i][e] = 0.0f;
+            acc[i][e] = kAcc0;
 
-    // Batches are unrolled up to the largest top-k the entry points accept,
-    // with a uniform exit: a loop with a run-time trip count makes the
-    // compiler wait for every earlier load before each gather.
-    constexpr int kSlotsMax = KC > 0 ? KC : KC < 0 ? -KC : kMaxTopK;
-#pragma unroll
-    for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
-        if (KC <= 0 && k0 >= top_k)
-            break;
-        // Uniform per-slot data first (scalar loads, one wait), then every
-        // valid slot's row vectors, then the FMAs in ascending slot order.
-        int64_t row_off[KB];   // elements
-        bool ok[KB];
-        float w[KB];
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            const int k = k0 + b;
-            // Slots past a run-time top-k re-read the token's last slot
-            // (always in bounds) and are masked: the metadata loads stay
-            // unconditional, so they issue together behind one wait.
-            const bool live = KC > 0 || k < top_k;
-            const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
-            if constexpr (L == Layout::kIndexMap) {
-                w[b] = load_weight<W_BF16>(a.weights, tk + kk);
-                const int32_t i = a.idx[tk + kk];
-                ok[b] = live && i >= 0 && (int64_t)i < a.num_rows;
-                row_off[b] = (int64_t)i * a.row_stride;
-            } else if constexpr (L == Layout::kTokenMajor) {
-                w[b] = load_weight<W_BF16>(a.weights, tk + kk);
-                ok[b] = live;
-                row_off[b] = (tk + kk) * (int64_t)a.hidden;
-            } else {   // kDirect: fma(1, x, +0) == x exactly
-                w[b] = 1.0f;
-                ok[b] = live;
-                row_off[b] = t * a.row_stride;
-            }
+    if constexpr (kRoll) {
+        constexpr int W = KB;
+        // Slot metadata in VGPRs: lane l of every wave holds slot l's index
+        // and weight (lanes past top-k an invalid index and weight 0), read
+        // back as scalars per slot.  The loads are unconditional: lanes past
+        // top-k re-read the last slot.
+        const int wl = lane & (kWave - 1);
+        const int64_t ms = tk + (wl < top_k ? wl : top_k - 1);
+        int32_t m_idx = -1;
+        if constexpr (kIdx)
+            m_idx = a.idx[ms];
+        float m_w = load_weight<W_BF16>(a.weights, ms);
+        if (wl >= top_k) {
+            m_idx = -1;
+            m_w = 0.0f;
         }
-        u32x4 v[KB][VPT];
+
+        u32x4 v[W][VPT];
+        float wt[W];
+        // The row address is computed whether or not the slot is valid (an
+        // empty resource never dereferences it): a select between it and a
+        // constant would be turned into a branch, and branches between the
+        // slots would let the compiler sink each slot's FMAs past the loads
+        // that follow them.
+        const uint64_t rows = reinterpret_cast<uintptr_t>(a.rows);
+        auto issue = [&](int s) {
+            const int b = s % W;
+            const float w = lane_value(m_w, s);
+            bool ok;
+            int64_t off;   // elements
+            if constexpr (kIdx) {
+                const int32_t i = lane_value(m_idx, s);
+                ok = i >= 0 && (int64_t)i < a.num_rows;
+                off = (int64_t)i * a.row_stride;
+            } else {
+                ok = KC > 0 || s < top_k;
+                off = (tk + s) * (int64_t)a.hidden;
+            }
+            wt[b] = ok ? w : 0.0f;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<void *>(rows + 2 * (uint64_t)off), 0, ok ? nv * 16 : 0,
+                kRawBufferWord3);
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (ok[b]) {
-                const u32x4 *r = reinterpret_cast<const u32x4 *>(a.rows + row_off[b]);
+            for (int i = 0; i < VPT; ++i)   // vectors past the row read as zeros
+                v[b][i] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + i * team) * 16, 0,
+                                                                MF_ROW_LOAD_POLICY);
+        };
 #pragma unroll
-                for (int i = 0; i < VPT; ++i) {
-                    const int j = lane + i * team;
-                    if (EXACT || j < nv)
-                        v[b][i] = load_row_vec(r + j);
-                    else
-                        v[b][i] = (u32x4){0u, 0u, 0u, 0u};
+        for (int s = 0; s < W; ++s)
+            issue(s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kSlotsMax; ++s) {
+            const int b = s % W;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[i][e] = __builtin_fmaf(wt[b], elem(v[b][i], e), acc[i][e]);
+                // An empty statement that reads and writes the sums keeps this
+                // slot's FMAs here: otherwise instruction selection may place
+                // every slot's FMAs after the last barrier, with all 32 slots'
+                // rows held in registers.
+                asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]),
+                             "+v"(acc[i][3]), "+v"(acc[i][4]), "+v"(acc[i][5]),
+                             "+v"(acc[i][6]), "+v"(acc[i][7]));
+            }
+            if (s + W < kSlotsMax)
+                issue(s + W);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // Batches of KB slots (one batch when every slot fits): uniform
+        // per-slot data first (scalar loads, one wait), then every valid
+        // slot's row vectors, then the FMAs in ascending slot order.  The
+        // batches are unrolled up to the slots the kernel serves, with a
+        // uniform exit past a run-time top-k.
+#pragma unroll
+        for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
+            if (KC < 0 && k0 >= top_k)
+                break;
+            int64_t row_off[KB];   // elements
+            bool ok[KB];
+            float w[KB];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                // Slots past a run-time top-k re-read the token's last slot
+                // (always in bounds) and are masked: the metadata loads stay
+                // unconditional, so they issue together behind one wait.
+                const int k = k0 + b;
+                const bool live = KC > 0 || k < top_k;
+                const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
+                if constexpr (kIdx) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                    const int32_t i = a.idx[tk + kk];
+                    ok[b] = live && i >= 0 && (int64_t)i < a.num_rows;
+                    row_off[b] = (int64_t)i * a.row_stride;
+                } else if constexpr (L == Layout::kTokenMajor) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                    ok[b] = live;
+                    row_off[b] = (tk + kk) * (int64_t)a.hidden;
+                } else {   // kDirect
+                    w[b] = 1.0f;
+                    ok[b] = live;
+                    row_off[b] = t * a.row_stride;
                 }
             }
-        }
+            u32x4 v[KB][VPT];
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (ok[b]) {
+            for (int b = 0; b < KB; ++b) {
+                if (ok[b]) {
+                    const u32x4 *r = reinterpret_cast<const u32x4 *>(a.rows + row_off[b]);
 #pragma unroll
-                for (int i = 0; i < VPT; ++i)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
+                    for (int i = 0; i < VPT; ++i) {
+                        const int j = lane + i * team;
+                        if (EXACT || j < nv)
+                            v[b][i] = load_row_vec(r + j);
+                        else
+                            v[b][i] = (u32x4){0u, 0u, 0u, 0u};
+                    }
+                }
             }
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (ok[b]) {
+#pragma unroll
+                    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
+                }
+            }
+            // Every gather of this batch has been consumed.  Saying so keeps
+            // the compiler, which cannot pair each conditional load with its
+            // conditional use, from waiting before each gather of the next
+            // batch.
+            if constexpr (kSlotsMax > KB)
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
-        // Every gather of this batch has been consumed.  Saying so keeps the
-        // compiler, which cannot pair each conditional load with its
-        // conditional use, from waiting before each gather of the next batch.
-        if constexpr (kSlotsMax > KB)
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     const __amdgpu_buffer_rsrc_t out_row =
@@ -512,69 +559,11 @@ finalize_kernel(const FinalizeArgs a)
 
 // ------------------------------------------------------------ dispatch ---
 
-// Whether `vpt` can be chosen at all: once a value that fits every even n
-// (VPT 1) appears in MF_VPT_ORDER, later entries are never picked, so their
-// kernels are not instantiated.
-constexpr bool vpt_reachable(int vpt)
+// Dynamic LDS that caps the resident workgroups per CU (plan.hpp), from the
+// device's LDS limits, queried once per device; concurrent first calls
+// store the same values.
+size_t residency_lds_bytes(int hidden, int slots)
 {
-    constexpr int order[] = {MF_VPT_ORDER};
-    for (int v : order) {
-        if (v == vpt)
-            return true;
-        if (v == 1)
-            return false;
-    }
-    return false;
-}
-
-// Whether a team of 32 n / vpt threads is a whole number of waves within the
-// launch bound of that vpt.
-inline bool team_fits(int n, int vpt)
-{
-    const int team = 32 * n / vpt;
-    const int bound = vpt == 1 ? 1024 : vpt == 2 ? 512 : 256;
-    return (32 * n) % vpt == 0 && team % kWave == 0 && team >= kWave && team <= bound;
-}
-
-// Vectors per thread for hidden = 256 n: one for index-map rows up to
-// MF_INDEX_MAP_VPT1_MAX_HIDDEN, else the first of MF_VPT_ORDER whose team
-// fits; 0 if none (then one vector per thread with the last half wave idle).
-// On the index map, a run-time top-k below 8 (kc < 0) widens that by
-// 8 / -kc where the team still fits, so a thread keeps about as many row
-// vectors in flight as at top-k 8 while workgroups stay small enough for
-// high occupancy (2-8 % faster at top-k 2 and 4; token-major rows measured
-// faster without it).
-inline int pick_vpt(Layout l, int n, int kc)
-{
-    int base = 0;
-    if (l == Layout::kIndexMap && 256 * n <= MF_INDEX_MAP_VPT1_MAX_HIDDEN && n % 2 == 0 &&
-        vpt_reachable(1)) {
-        base = 1;
-    } else {
-        for (int vpt : {MF_VPT_ORDER})
-            if (team_fits(n, vpt)) {
-                base = vpt;
-                break;
-            }
-    }
-    if (l == Layout::kIndexMap && kc < 0 && base > 0)
-        for (int vpt = std::min(8, base * 8 / -kc); vpt > base; vpt /= 2)
-            if (team_fits(n, vpt))
-                return vpt;
-    return base;
-}
-
-// Dynamic LDS to reserve per workgroup so that a CU holds
-// ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup) workgroups,
-// clamped to 2..16.  Beyond that, extra concurrent gathers do not raise
-// bandwidth; they stretch every token's lifetime and with it the tail of
-// the launch (measured: 2-5 % faster on every large workload than residency
-// limited by registers).  The kernels' own LDS use is 64 bytes.
-inline size_t residency_lds(int hidden, int slots)
-{
-#if MF_INFLIGHT_KB_PER_CU > 0
-    // Per-device LDS limits, queried once; concurrent first calls store the
-    // same values.
     static std::atomic<int> lds_per_cu[64], lds_per_block[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
@@ -590,78 +579,81 @@ inline size_t residency_lds(int hidden, int slots)
         lds_per_cu[dev].store(cu, std::memory_order_relaxed);
         lds_per_block[dev].store(blk, std::memory_order_relaxed);
     }
-    const int64_t per_block = 2LL * hidden * slots;           // row bytes in flight
-    const int64_t want = ((int64_t)MF_INFLIGHT_KB_PER_CU * 1024 + per_block - 1) / per_block;
-    const int64_t blocks = std::min<int64_t>(16, std::max<int64_t>(2, want));
-    const int64_t lds = std::min<int64_t>(cu / blocks - 1024, blk);
-    return lds > 0 ? (size_t)lds : 0;
-#else
-    (void)hidden;
-    (void)slots;
-    return 0;
-#endif
+    return (size_t)residency_lds(hidden, slots, cu, blk, kStaticLds);
 }
 
+// Launch the kernel of plan p over all tokens, at most p.max_tokens per
+// launch (each launch starts at its token_base).
 template <Layout L, bool W_BF16, Epilogue EPI, int KC>
-hipError_t launch_shape(const FinalizeArgs &a, hipStream_t s)
+hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s)
 {
-    if (a.top_k < 1 || a.top_k > kMaxTopK || (KC > 0 && a.top_k != KC) ||
-        (KC < 0 && a.top_k > -KC))
-        return hipErrorInvalidValue;
-    const int n = a.hidden / 256;
-    const int nv = 32 * n;
-    const dim3 grid((unsigned)a.num_tokens);
-    const int vpt = pick_vpt(L, n, KC);
-    // Slots actually in flight: with top-k read at run time the batch may be
-    // larger than top-k, and the cap must follow the rows really fetched.
-    const int slots = std::min(KC > 0 ? KC : a.top_k, slots_in_flight(L, KC, vpt > 0 ? vpt : 1));
-    const size_t lds = residency_lds(a.hidden, slots);
-    switch (vpt) {
-    case 8:
-        if constexpr (vpt_reachable(8) || KC < 0)
-            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid,
-                               dim3(nv / 8), lds, s, a);
-        break;
-    case 4:
-        if constexpr (vpt_reachable(4) || KC < 0)
-            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid,
-                               dim3(nv / 4), lds, s, a);
-        break;
-    case 2:
-        if constexpr (vpt_reachable(2) || KC < 0)
-            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid,
-                               dim3(nv / 2), lds, s, a);
-        break;
-    case 1:
-        if constexpr (vpt_reachable(1) || KC < 0)
-            hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid,
-                               dim3(nv), lds, s, a);
-        break;
-    default:   // n odd: 32 (n + 1) threads, the last half wave idle
-        hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false>), grid,
-                           dim3(nv + 32), lds, s, a);
-        break;
+    const size_t lds = residency_lds_bytes(a.hidden, p.slots);
+    FinalizeArgs c = a;
+    for (int64_t t0 = 0; t0 < a.num_tokens; t0 += p.max_tokens) {
+        c.token_base = t0;
+        const dim3 grid((unsigned)std::min<int64_t>(p.max_tokens, a.num_tokens - t0));
+        const dim3 block((unsigned)p.team);
+        switch (p.vpt) {
+        case 8:
+            if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 8))
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid, block,
+                                   lds, s, c);
+            break;
+        case 4:
+            if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 4))
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid, block,
+                                   lds, s, c);
+            break;
+        case 2:
+            if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 2))
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid, block,
+                                   lds, s, c);
+            break;
+        case 1:
+            if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 1))
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid, block,
+                                   lds, s, c);
+            break;
+        default:   // n odd: 32 (n + 1) threads, the last half wave idle
+            if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 0))
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false>), grid, block,
+                                   lds, s, c);
+            break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-// Compile-time slot counts for the common top-k values; other top-k read at
-// run time, by a kernel sized for 8 slots up to 8, in batches beyond.
+// Compile-time slot counts for the common top-k values (8, 16); other top-k
+// are read at run time by kernels sized for 2, 4, 8, 12, 16, 24 or 32 slots.
 template <Layout L, bool W_BF16, Epilogue EPI>
 hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
 {
-    switch (a.top_k) {
+    const LaunchPlan p = plan_launch(L == Layout::kIndexMap, false, a.hidden, a.top_k);
+    switch (p.kc) {
     case 8:
-        return launch_shape<L, W_BF16, EPI, 8>(a, s);
+        return launch_plan<L, W_BF16, EPI, 8>(a, p, s);
     case 16:
-        return launch_shape<L, W_BF16, EPI, 16>(a, s);
+        return launch_plan<L, W_BF16, EPI, 16>(a, p, s);
+    case -2:
+        return launch_plan<L, W_BF16, EPI, -2>(a, p, s);
+    case -4:
+        return launch_plan<L, W_BF16, EPI, -4>(a, p, s);
+    case -8:
+        return launch_plan<L, W_BF16, EPI, -8>(a, p, s);
+    case -12:
+        return launch_plan<L, W_BF16, EPI, -12>(a, p, s);
+    case -16:
+        return launch_plan<L, W_BF16, EPI, -16>(a, p, s);
+    case -24:
+        return launch_plan<L, W_BF16, EPI, -24>(a, p, s);
+    case -32:
+        return launch_plan<L, W_BF16, EPI, -32>(a, p, s);
     default:
-        if (a.top_k <= 2)
-            return launch_shape<L, W_BF16, EPI, small_topk_kc(2)>(a, s);
-        if (a.top_k <= 4)
-            return launch_shape<L, W_BF16, EPI, small_topk_kc(4)>(a, s);
-        return a.top_k < 8 ? launch_shape<L, W_BF16, EPI, small_topk_kc(7)>(a, s)
-                           : launch_shape<L, W_BF16, EPI, 0>(a, s);
+        return hipErrorInvalidValue;
     }
 }
 
@@ -672,10 +664,17 @@ hipError_t launch_index_map(const FinalizeArgs &a, hipStream_t s)
                           : launch_topk<Layout::kIndexMap, false, EPI>(a, s);
 }
 
-}  // namespace
-
-hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, hipStream_t s)
+template <Epilogue EPI>
+hipError_t launch_direct(const FinalizeArgs &a, hipStream_t s)
 {
+    return launch_plan<Layout::kDirect, false, EPI, 1>(
+        a, plan_launch(false, true, a.hidden, 1), s);
+}
+
+hipError_t dispatch(const FinalizeArgs &a, Layout layout, Epilogue epi, hipStream_t s)
+{
+    if (a.top_k < 1 || a.top_k > kMaxTopK || a.num_tokens < 0)
+        return hipErrorInvalidValue;
     switch (layout) {
     case Layout::kIndexMap:
         switch (epi) {
@@ -704,17 +703,29 @@ hipError_t launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, h
     case Layout::kDirect:
         switch (epi) {
         case Epilogue::kRmsNorm:
-            return launch_shape<Layout::kDirect, false, Epilogue::kRmsNorm, 1>(a, s);
+            return launch_direct<Epilogue::kRmsNorm>(a, s);
         case Epilogue::kRmsNormWeightFirst:
-            return launch_shape<Layout::kDirect, false, Epilogue::kRmsNormWeightFirst, 1>(a, s);
+            return launch_direct<Epilogue::kRmsNormWeightFirst>(a, s);
         case Epilogue::kResidualNorm:
-            return launch_shape<Layout::kDirect, false, Epilogue::kResidualNorm, 1>(a, s);
+            return launch_direct<Epilogue::kResidualNorm>(a, s);
         default:
             break;
         }
         break;
     }
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, void *stream)
+{
+    return static_cast<int>(dispatch(a, layout, epi, static_cast<hipStream_t>(stream)));
+}
+
+const char *launch_error_string(int code)
+{
+    return hipGetErrorString(static_cast<hipError_t>(code));
 }
 
 }  // namespace mf

@@ -1,0 +1,228 @@
+// Launch planning shared by the gfx950 kernels (as compile-time constants)
+// and the host launcher (finalize_kernels.hip): team shape, slots in flight,
+// residency and the split of a call into launches.  Plain C++ with no HIP
+// types, so host tests can check the arithmetic on the CPU.
+#pragma once
+
+#include <stdint.h>
+
+// Row vectors in flight per thread.  16 (64 VGPRs) keeps two workgroups per
+// CU at two vectors per thread; 32 had let an index-map top-k 16 token have
+// all its rows in flight, but at hidden above 4096 the 150-160 VGPRs that
+// takes leave one workgroup per CU (hidden 5120-8192, top-k 12-16: 3-11 %
+// slower than batches of 8).  A token-major token is one contiguous block,
+// also faster fetched in halves (top-k 16: 10 % faster than all at once).
+#ifndef MF_MAX_VECS_INDEX_MAP
+#define MF_MAX_VECS_INDEX_MAP 16
+#endif
+#ifndef MF_MAX_VECS_TOKEN_MAJOR
+#define MF_MAX_VECS_TOKEN_MAJOR 16
+#endif
+#ifndef MF_VPT_ORDER
+#define MF_VPT_ORDER 2, 1, 4, 8 // preferred vectors per thread, first that fits
+#endif
+// Index-map rows up to this hidden size take one vector per thread instead
+// (teams of up to 512 threads): 1 % faster at 8192 tokens and hidden 4096,
+// 5 % at 256 tokens, 3 % at hidden 2048 / top-k 16; at hidden 7168 the
+// 896-thread teams are 5 % slower, and token-major tokens prefer two
+// vectors per thread at every size measured.  0 disables the override.
+#ifndef MF_INDEX_MAP_VPT1_MAX_HIDDEN
+#define MF_INDEX_MAP_VPT1_MAX_HIDDEN 4096
+#endif
+// Where a token has more slots than fit in flight at once, index-map slots
+// stream through a rolling window of this many slots (by vectors per thread:
+// one, two), and token-major slots arrive in batches (a token's rows are one
+// contiguous block, fetched fastest in bursts: a rolling window measured 4 %
+// slower at top-k 16 and hidden 2048, and no faster at any other shape).
+#ifndef MF_ROLL_INDEX_MAP
+#define MF_ROLL_INDEX_MAP 1
+#endif
+#ifndef MF_ROLL_TOKEN_MAJOR
+#define MF_ROLL_TOKEN_MAJOR 0
+#endif
+#ifndef MF_ROLL_WINDOW_VPT1
+#define MF_ROLL_WINDOW_VPT1 16
+#endif
+#ifndef MF_ROLL_WINDOW_VPT2
+#define MF_ROLL_WINDOW_VPT2 8
+#endif
+#ifndef MF_INFLIGHT_KB_PER_CU
+#define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
+                                  // loads in flight total about this much per CU
+#endif
+
+namespace mf {
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 32;   // the entry points reject larger top-k
+constexpr int kMaxWaves = 16;
+// Work-items one launch may span.  The dispatch packet counts the grid in
+// 32-bit work-items; a call whose tokens need more is split into launches of
+// at most this many (2^31, which also keeps every runtime-side product of
+// grid and team inside a signed 32-bit integer).
+constexpr int64_t kMaxThreadsPerLaunch = int64_t(1) << 31;
+
+inline constexpr int layout_max_vecs(bool index_map)
+{
+    return index_map ? MF_MAX_VECS_INDEX_MAP : MF_MAX_VECS_TOKEN_MAJOR;
+}
+
+// Row vectors one thread keeps in flight.  One vector per thread means teams
+// of up to 1024 threads, whose launch bound leaves 128 VGPRs per thread: at
+// most 16 vectors (64 VGPRs) there.
+constexpr int max_vecs(bool index_map, int vpt)
+{
+    return vpt == 1 && layout_max_vecs(index_map) > 16 ? 16 : layout_max_vecs(index_map);
+}
+
+// Slot-count template argument:
+//   KC > 0   top-k is KC (8 and 16);
+//   KC < 0   top-k is read at run time and is at most -KC; registers are
+//            sized for -KC slots, so a small top-k keeps a small register
+//            footprint and high occupancy, and a larger one wastes at most a
+//            few slots (-2, -4, -8, -12, -16, -24, -32).
+constexpr int small_topk_kc(int top_k) { return top_k <= 2 ? -2 : top_k <= 4 ? -4 : -8; }
+
+// The KC a top-k is served by.
+constexpr int kc_for_topk(int top_k)
+{
+    return top_k == 8 ? 8 : top_k == 16 ? 16 : top_k < 8 ? small_topk_kc(top_k)
+         : top_k <= 12 ? -12 : top_k <= 16 ? -16 : top_k <= 24 ? -24 : -32;
+}
+
+constexpr bool streams(bool index_map) { return index_map ? MF_ROLL_INDEX_MAP : MF_ROLL_TOKEN_MAJOR; }
+
+// Whether a token's slots stream through a rolling window instead of
+// arriving in one batch or in several: more slots than fit in flight, on a
+// layout that streams.
+constexpr bool rolling(bool index_map, int kc, int vpt)
+{
+    return streams(index_map) && (kc < 0 ? -kc : kc) * vpt > max_vecs(index_map, vpt);
+}
+
+// Slots whose rows one workgroup has in flight at once: all -KC (or KC) when
+// they fit in max_vecs, else the rolling window, else batches of max_vecs /
+// VPT slots.
+constexpr int slots_in_flight(bool index_map, int kc, int vpt)
+{
+    const int want = kc < 0 ? -kc : kc;
+    if (want * vpt <= max_vecs(index_map, vpt))
+        return want;
+    if (rolling(index_map, kc, vpt))
+        return vpt == 1 ? MF_ROLL_WINDOW_VPT1 : vpt == 2 ? MF_ROLL_WINDOW_VPT2
+                                                          : max_vecs(index_map, vpt) / vpt;
+    return max_vecs(index_map, vpt) / vpt;
+}
+
+constexpr int max_team(int vpt) { return vpt == 1 ? 1024 : vpt == 2 ? 512 : 256; }
+
+// Whether `vpt` can be chosen at all: once a value that fits every even n
+// (VPT 1) appears in MF_VPT_ORDER, later entries are never picked, so their
+// kernels are not instantiated.
+constexpr bool vpt_reachable(int vpt)
+{
+    constexpr int order[] = {MF_VPT_ORDER};
+    for (int v : order) {
+        if (v == vpt)
+            return true;
+        if (v == 1)
+            return false;
+    }
+    return false;
+}
+
+// Whether a team of 32 n / vpt threads is a whole number of waves within the
+// launch bound of that vpt.
+constexpr bool team_fits(int n, int vpt)
+{
+    return (32 * n) % vpt == 0 && (32 * n / vpt) % kWave == 0 && 32 * n / vpt >= kWave &&
+           32 * n / vpt <= max_team(vpt);
+}
+
+// Vectors per thread for hidden = 256 n: one for index-map rows up to
+// MF_INDEX_MAP_VPT1_MAX_HIDDEN, else the first of MF_VPT_ORDER whose team
+// fits; 0 if none (then one vector per thread with the last half wave idle).
+// On the index map, a run-time top-k below 8 (kc < 0) widens that by
+// 8 / -kc where the team still fits, so a thread keeps about as many row
+// vectors in flight as at top-k 8 while workgroups stay small enough for
+// high occupancy (2-8 % faster at top-k 2 and 4; token-major rows measured
+// faster without it).
+constexpr int pick_vpt(bool index_map, int n, int kc)
+{
+    int base = 0;
+    if (index_map && 256 * n <= MF_INDEX_MAP_VPT1_MAX_HIDDEN && n % 2 == 0 && vpt_reachable(1)) {
+        base = 1;
+    } else {
+        constexpr int order[] = {MF_VPT_ORDER};
+        for (int vpt : order)
+            if (team_fits(n, vpt)) {
+                base = vpt;
+                break;
+            }
+    }
+    if (index_map && kc < 0 && base > 0)
+        for (int vpt = (base * 8 / -kc < 8 ? base * 8 / -kc : 8); vpt > base; vpt /= 2)
+            if (team_fits(n, vpt))
+                return vpt;
+    return base;
+}
+
+// Whether pick_vpt returns `vpt` for some hidden size of the envelope
+// (256 n, n = 1..32): kernels for other values are not instantiated.
+constexpr bool vpt_possible(bool index_map, int kc, int vpt)
+{
+    for (int n = 1; n <= 32; ++n)
+        if (pick_vpt(index_map, n, kc) == vpt)
+            return true;
+    return false;
+}
+
+// How one call is launched.
+struct LaunchPlan {
+    int kc;               // slot-count template argument
+    int vpt;              // 16-byte vectors per thread (0: one, last half wave idle)
+    int team;             // threads per workgroup (one token each)
+    int slots;            // slots whose rows a workgroup has in flight at once
+    bool exact;           // hidden / 8 == team * vpt
+    int64_t max_tokens;   // tokens per launch at most
+};
+
+constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int top_k)
+{
+    LaunchPlan p{};
+    const int n = hidden / 256;
+    p.kc = direct ? 1 : kc_for_topk(top_k);
+    p.vpt = pick_vpt(index_map, n, p.kc);
+    p.exact = p.vpt > 0;
+    p.team = p.vpt > 0 ? 32 * n / p.vpt : 32 * n + 32;
+    const int kk = p.kc > 0 ? p.kc : top_k;
+    const int win = slots_in_flight(index_map, p.kc, p.vpt > 0 ? p.vpt : 1);
+    p.slots = kk < win ? kk : win;
+    p.max_tokens = kMaxThreadsPerLaunch / p.team;
+    return p;
+}
+
+// Dynamic LDS to reserve per workgroup so that a CU holds
+// ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup) workgroups,
+// clamped to 2..16, given the device's LDS per CU and per workgroup and the
+// kernel's own static LDS.  Beyond that, extra concurrent gathers do not
+// raise bandwidth; they stretch every token's lifetime and with it the tail
+// of the launch (measured: 2-5 % faster on every large workload than
+// residency limited by registers).  0 when no cap applies.
+constexpr int64_t residency_lds(int hidden, int slots, int64_t lds_per_cu,
+                                int64_t lds_per_block, int64_t static_lds)
+{
+    if (MF_INFLIGHT_KB_PER_CU <= 0 || lds_per_cu <= 0 || lds_per_block <= 0)
+        return 0;
+    const int64_t per_block = 2LL * hidden * slots;   // row bytes in flight
+    const int64_t want = ((int64_t)MF_INFLIGHT_KB_PER_CU * 1024 + per_block - 1) / per_block;
+    const int64_t blocks = want < 2 ? 2 : want > 16 ? 16 : want;
+    // Leave 1 KiB of the CU's share unclaimed, and never ask for more than a
+    // workgroup may hold besides the kernel's own LDS.
+    int64_t lds = lds_per_cu / blocks - 1024;
+    if (lds > lds_per_block - static_lds)
+        lds = lds_per_block - static_lds;
+    return lds > 0 ? lds : 0;
+}
+
+}  // namespace mf

@@ -102,3 +102,41 @@ def test_threaded_oracle_baseline_covers_every_token():
     whole = fake.cpu_oracle(oracle, slice(0, 37))[0]
     parts = [fake.cpu_oracle(oracle, slice(a, b))[0] for a, b in ((0, 5), (5, 20), (20, 37))]
     assert np.array_equal(np.concatenate(parts), whole)
+
+
+def test_agreement_stats():
+    got = np.array([0x3F80, 0x3F81, 0x7FC0, 0x0000, 0x4000], np.uint16)
+    want = np.array([0x3F80, 0x3F80, 0x3F80, 0x8000, 0x4002], np.uint16)
+    a = bench.agreement_stats([(got, want)])
+    assert a["elements"] == 5 and a["nan_outputs"] == 1
+    assert a["max_ulp"] == 1 << 20                       # NaN against a number
+    assert a["bit_exact_fraction"] == 2 / 5              # 0x3F80 and +0 == -0
+    assert a["within_1_ulp_fraction"] == 3 / 5
+
+
+@pytest.mark.parametrize("config,ratio", [
+    (dict(T=8192, K=8, H=4096, kind="index"), 8),
+    (dict(T=16000, K=16, H=2048, kind="token"), 16),
+    (dict(T=3000, K=8, H=7168, kind="token"), 8),
+    (dict(T=16000, K=16, H=2048, kind="residual"), 8),
+])
+def test_practical_ceiling_uses_the_workloads_mix(config, ratio):
+    """The mixed probe reads as many vectors per write as the workload does
+    (nearest of 4, 8, 16): 8 at top-k 8, 16 at top-k 16, and 8.5 -> 8 for the
+    residual variant, which also reads the residual and writes two rows."""
+    T, K, H = config["T"], config["K"], config["H"]
+    if config["kind"] == "index":
+        fake = SimpleNamespace(c=index_map_shape(T, K, H, "fp32"))
+        fake.bytes = bench.index_map_bytes(fake.c, norm=True)
+        r = bench.IndexMapBench.read_write_ratio(fake)
+    elif config["kind"] == "token":
+        fake = SimpleNamespace(c=SimpleNamespace(live_tokens=T, top_k=K, hidden=H,
+                                                 post_weight=None))
+        fake.bytes = bench.token_major_bytes(fake.c)
+        r = bench.TokenMajorBench.read_write_ratio(fake)
+    else:
+        fake = SimpleNamespace(c=SimpleNamespace(live_tokens=T, top_k=K, hidden=H))
+        fake.bytes = T * K * H * 2 + T * H * 2 * 3 + T * K * 4 + 2 * H * 2
+        r = bench.ResidualBench.read_write_ratio(fake)
+    assert bench.probe_ratio(r) == ratio
+

@@ -1,10 +1,10 @@
 """Host-side tests of the C ABI (no GPU needed).
 
-The library must load, export every function include/moe_finalize.h
-declares, and reject bad arguments with the documented status before any HIP
-call.  Zero-row calls return MF_OK without launching.  The pointers used
-here are never dereferenced: every call below fails validation or has
-nothing to do.
+The library must load and export every function include/moe_finalize.h
+declares, with the binding's prototypes matching the header.  Argument
+validation, the launch plan and the split of large token counts into
+launches run against the host-check build of the same C ABI code, whose
+launcher is a recording stand-in: nothing here can reach a GPU.
 """
 import ctypes
 import os
@@ -12,14 +12,12 @@ import re
 
 import pytest
 
+import capi_cases as cc
 import moe_expert_output_finalize_amd as mf
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_finalize.h")
-
-OK, NULLP, SHAPE, DTYPE, ALIGN, ARG = 0, 1, 2, 3, 4, 5
-BF16, FP32 = 1, 2
-P = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+HOSTCHECK = os.path.join(ROOT, "tests", "libmf_hostcheck.so")
 
 
 def declared_functions():
@@ -79,135 +77,105 @@ def test_status_strings():
     assert mf.lib.mf_last_error_message().decode() == ""
 
 
-def rmsnorm(**over):
-    a = dict(g=P, rows=128, stride=4096, w=P, wdt=FP32, idx=P, nw=P, out=P, T=16, H=4096, K=8,
-             eps=1e-6, gc=1.0, wbn=0, stream=None)
-    a.update(over)
-    return mf.lib.moe_finalize_rmsnorm(a["g"], a["rows"], a["stride"], a["w"], a["wdt"],
-                                       a["idx"], a["nw"], a["out"], a["T"], a["H"], a["K"],
-                                       a["eps"], a["gc"], a["wbn"], a["stream"])
+# ------------------------------------------- validation (no GPU involved) ---
+#
+# The cases run against tests/libmf_hostcheck.so: the same C ABI host code
+# (csrc/capi.cpp) as the real library, linked with a recording stand-in for
+# the launcher instead of the HIP kernels, so a case that validation wrongly
+# accepts is recorded, never launched.
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(HOSTCHECK):
+        pytest.fail(f"{HOSTCHECK} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(HOSTCHECK)
+    cc.declare(lib)
+    lib.mf_test_record.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    lib.mf_test_fail_next_launch.argtypes = [ctypes.c_int]
+    lib.mf_last_error_message.restype = ctypes.c_char_p
+    return lib
 
 
-def finalize(**over):
-    a = dict(g=P, rows=128, stride=4096, w=P, wdt=FP32, idx=P, out=P, T=16, H=4096, K=8,
-             stream=None)
-    a.update(over)
-    return mf.lib.moe_finalize(a["g"], a["rows"], a["stride"], a["w"], a["wdt"], a["idx"],
-                               a["out"], a["T"], a["H"], a["K"], a["stream"])
+def record(lib) -> dict:
+    buf = (ctypes.c_int64 * 12)()
+    lib.mf_test_record(buf)
+    keys = ("calls", "layout", "epi", "num_tokens", "hidden", "top_k", "kc", "vpt", "team",
+            "launches", "max_tokens", "violations")
+    return dict(zip(keys, list(buf)))
 
 
-def beam(**over):
-    a = dict(e=P, cap=4096, K=8, H=7168, w=P, wrows=4096, out=P, live=3000, pw=None,
-             scale=2.5, eps=0.0, norm=0, stream=None)
-    a.update(over)
-    return mf.lib.beam_moe_finalize(a["e"], a["cap"], a["K"], a["H"], a["w"], a["wrows"],
-                                    a["out"], a["live"], a["pw"], a["scale"], a["eps"],
-                                    a["norm"], a["stream"])
+@pytest.mark.parametrize("case", cc.CASES, ids=cc.case_id)
+def test_validation(host, case):
+    """Each invalid argument is rejected with its status and launches
+    nothing; each valid call launches exactly once with arguments the
+    kernels can use, and zero-row calls launch nothing."""
+    fn, over, want = case
+    host.mf_test_reset()
+    assert cc.ctypes_call(host, fn, over) == want
+    rec = record(host)
+    zero_rows = any(over.get(k) == 0 for k in ("T", "live"))
+    assert rec["calls"] == (1 if want == cc.OK and not zero_rows else 0)
+    assert rec["violations"] == 0
 
 
-# Each case would be valid but for the one named change; T = 0 keeps the
-# valid base from launching anything.
-@pytest.mark.parametrize("over,want", [
-    (dict(T=0), OK),
-    (dict(T=0, g=None, w=None, idx=None, nw=None, out=None), OK),
-    (dict(T=0, H=2048, K=4), OK), (dict(T=0, H=256, K=1), OK), (dict(T=0, H=8192, K=32, stride=8192), OK),
-    (dict(H=2000), SHAPE), (dict(H=8448, stride=8448), SHAPE), (dict(K=0), SHAPE), (dict(K=33), SHAPE),
-    (dict(T=-1), SHAPE), (dict(rows=-1), SHAPE),
-    (dict(T=1 << 31), SHAPE), (dict(stride=4088), SHAPE),
-    (dict(stride=4100), ALIGN), (dict(wdt=0), DTYPE), (dict(wdt=3), DTYPE),
-    (dict(g=None), NULLP), (dict(w=None), NULLP), (dict(idx=None), NULLP),
-    (dict(nw=None), NULLP), (dict(out=None), NULLP),
-    (dict(g=P + 2), ALIGN), (dict(w=P + 4), ALIGN), (dict(idx=P + 8), ALIGN),
-    (dict(nw=P + 2), ALIGN), (dict(out=P + 8), ALIGN),
+@pytest.mark.parametrize("case", cc.SPLIT_CASES, ids=cc.case_id)
+def test_token_counts_beyond_one_launch_are_split(host, case):
+    """Calls whose grid would pass 2^31 work-items are split into launches
+    that each fit, cover every token once and keep the call's plan."""
+    fn, over, launches = case
+    host.mf_test_reset()
+    assert cc.ctypes_call(host, fn, over) == cc.OK
+    rec = record(host)
+    assert rec["calls"] == 1 and rec["violations"] == 0
+    assert rec["launches"] == launches
+    assert rec["max_tokens"] * rec["team"] <= 2 ** 31
+    assert (rec["launches"] - 1) * rec["max_tokens"] < rec["num_tokens"]
+    assert rec["launches"] * rec["max_tokens"] >= rec["num_tokens"]
+
+
+def test_largest_token_count_at_every_hidden_size(host):
+    """INT32_MAX tokens at every hidden size of the envelope and several top-k
+    on both layouts: accepted, and split into launches within the limit."""
+    for H in range(256, 8193, 256):
+        for K in (1, 5, 8, 13, 16, 32):
+            for fn, over in (("moe_finalize", dict(H=H, stride=H, K=K, T=cc.INT32_MAX)),
+                             ("beam_moe_finalize", dict(H=H, K=K, cap=cc.INT32_MAX,
+                                                        wrows=cc.INT32_MAX,
+                                                        live=cc.INT32_MAX))):
+                host.mf_test_reset()
+                assert cc.ctypes_call(host, fn, over) == cc.OK, (fn, H, K)
+                rec = record(host)
+                assert rec["violations"] == 0 and rec["calls"] == 1, (fn, H, K, rec)
+                assert rec["max_tokens"] * rec["team"] <= 2 ** 31
+
+
+@pytest.mark.parametrize("fn,over,kc,vpt,team", [
+    ("moe_finalize_rmsnorm", dict(), 8, 1, 512),
+    ("moe_finalize_rmsnorm", dict(H=7168, stride=7168, K=32), -32, 2, 448),
+    ("moe_finalize_rmsnorm", dict(H=2048, stride=2048, K=12), -12, 1, 256),
+    ("moe_finalize_rmsnorm", dict(H=4096, K=2), -2, 4, 128),
+    ("moe_finalize", dict(H=256, stride=256, K=1), -2, 0, 64),
+    ("beam_moe_finalize", dict(), 8, 2, 448),
+    ("beam_moe_finalize", dict(K=17), -24, 2, 448),
+    ("mf_rmsnorm", dict(), 1, 2, 256),
 ])
-def test_rmsnorm_validation(over, want):
-    assert rmsnorm(**over) == want
+def test_launch_plan(host, fn, over, kc, vpt, team):
+    """The kernel variant and team the launcher picks for a few shapes."""
+    host.mf_test_reset()
+    assert cc.ctypes_call(host, fn, over) == cc.OK
+    rec = record(host)
+    assert (rec["kc"], rec["vpt"], rec["team"]) == (kc, vpt, team), rec
 
 
-@pytest.mark.parametrize("over,want", [
-    (dict(T=0), OK), (dict(T=0, H=256, K=1), OK), (dict(T=0, H=8192, K=32, stride=8192), OK),
-    (dict(T=0, rows=0, g=None), OK),
-    (dict(H=128), SHAPE), (dict(H=8448, stride=8448), SHAPE), (dict(H=4000), SHAPE),
-    (dict(K=0), SHAPE), (dict(K=33), SHAPE), (dict(stride=2048, H=4096), SHAPE),
-    (dict(stride=4100), ALIGN), (dict(wdt=7), DTYPE),
-    (dict(out=None), NULLP), (dict(g=None), NULLP), (dict(g=P + 4), ALIGN),
-])
-def test_finalize_validation(over, want):
-    assert finalize(**over) == want
-
-
-@pytest.mark.parametrize("over,want", [
-    (dict(live=0), OK), (dict(live=0, e=None, w=None, out=None), OK),
-    (dict(live=0, norm=1, pw=P, eps=1e-6), OK),
-    (dict(K=0), SHAPE), (dict(K=33), SHAPE), (dict(H=7000), SHAPE), (dict(H=0), SHAPE),
-    (dict(H=8448), SHAPE), (dict(live=4097), SHAPE), (dict(wrows=2999), SHAPE),
-    (dict(cap=-1), SHAPE), (dict(live=-1), SHAPE),
-    (dict(pw=P, norm=0), ARG), (dict(e=None), NULLP), (dict(w=None), NULLP),
-    (dict(out=None), NULLP), (dict(e=P + 8), ALIGN), (dict(w=P + 2), ALIGN),
-    (dict(out=P + 2), ALIGN), (dict(pw=P + 2, norm=1), ALIGN),
-])
-def test_beam_validation(over, want):
-    assert beam(**over) == want
-
-
-def norm(**over):
-    a = dict(x=P, stride=4096, nw=P, out=P, T=16, H=4096, eps=1e-6, gc=1.0, wbn=0, stream=None)
-    a.update(over)
-    return mf.lib.mf_rmsnorm(a["x"], a["stride"], a["nw"], a["out"], a["T"], a["H"], a["eps"],
-                             a["gc"], a["wbn"], a["stream"])
-
-
-@pytest.mark.parametrize("over,want", [
-    (dict(T=0), OK), (dict(T=0, x=None, nw=None, out=None), OK), (dict(T=0, H=256), OK),
-    (dict(H=200), SHAPE), (dict(H=8448, stride=8448), SHAPE), (dict(T=-1), SHAPE),
-    (dict(stride=4000), SHAPE), (dict(stride=4100), ALIGN),
-    (dict(x=None), NULLP), (dict(nw=None), NULLP), (dict(out=None), NULLP),
-    (dict(x=P + 2), ALIGN), (dict(nw=P + 8), ALIGN), (dict(out=P + 4), ALIGN),
-])
-def test_standalone_norm_validation(over, want):
-    assert norm(**over) == want
-
-
-def fused_rn(**over):
-    a = dict(e=P, cap=16384, K=16, H=2048, w=P, wrows=16384, res=P, pw=P, nw=P, hid=P, nrm=P,
-             T=16000, scale=1.0, peps=1e-6, neps=1e-6, sx=1.0, sr=1.0, hp=1, hn=1, stream=None)
-    a.update(over)
-    return mf.lib.beam_moe_finalize_norm_residual_norm(
-        a["e"], a["cap"], a["K"], a["H"], a["w"], a["wrows"], a["res"], a["pw"], a["nw"], a["hid"],
-        a["nrm"], a["T"], a["scale"], a["peps"], a["neps"], a["sx"], a["sr"], a["hp"], a["hn"],
-        a["stream"])
-
-
-@pytest.mark.parametrize("over,want", [
-    (dict(T=0), OK), (dict(T=0, e=None, w=None, res=None, hid=None, nrm=None), OK),
-    (dict(K=0), SHAPE), (dict(K=33), SHAPE), (dict(H=2100), SHAPE), (dict(T=16385), SHAPE),
-    (dict(wrows=15999), SHAPE), (dict(cap=-1), SHAPE), (dict(T=-1), SHAPE),
-    (dict(hp=0), ARG), (dict(hn=0), ARG),
-    (dict(e=None), NULLP), (dict(w=None), NULLP), (dict(res=None), NULLP), (dict(hid=None), NULLP),
-    (dict(nrm=None), NULLP), (dict(res=P + 2), ALIGN), (dict(nw=P + 2), ALIGN),
-    (dict(hid=P + 8), ALIGN), (dict(nrm=P + 4), ALIGN), (dict(e=P + 2), ALIGN),
-])
-def test_fused_residual_norm_validation(over, want):
-    assert fused_rn(**over) == want
-
-
-def consumer(**over):
-    a = dict(x=P, stride=2048, res=P, pw=None, nw=P, hid=P, nrm=P, T=100, H=2048, peps=0.0,
-             neps=1e-6, sx=1.0, sr=1.0, hp=0, hn=1, stream=None)
-    a.update(over)
-    return mf.lib.beam_norm_residual_norm(
-        a["x"], a["stride"], a["res"], a["pw"], a["nw"], a["hid"], a["nrm"], a["T"], a["H"],
-        a["peps"], a["neps"], a["sx"], a["sr"], a["hp"], a["hn"], a["stream"])
-
-
-@pytest.mark.parametrize("over,want", [
-    (dict(T=0), OK), (dict(T=0, hn=0, nw=None, nrm=None, x=None, res=None, hid=None), OK),
-    (dict(H=100), SHAPE), (dict(stride=1024), SHAPE), (dict(stride=2052), ALIGN),
-    (dict(pw=P), ARG), (dict(hn=0), ARG), (dict(x=None), NULLP), (dict(res=None), NULLP),
-    (dict(hid=None), NULLP), (dict(nrm=None), NULLP), (dict(x=P + 2), ALIGN),
-])
-def test_consumer_validation(over, want):
-    assert consumer(**over) == want
+def test_failed_launch_is_reported(host):
+    """A launch error becomes MF_ERR_LAUNCH_FAILED with a message, which the
+    next successful call clears."""
+    host.mf_test_reset()
+    host.mf_test_fail_next_launch(98)
+    assert cc.ctypes_call(host, "moe_finalize", {}) == cc.LAUNCH
+    assert host.mf_last_error_message().decode().startswith("kernel launch failed")
+    assert cc.ctypes_call(host, "moe_finalize", {}) == cc.OK
+    assert host.mf_last_error_message().decode() == ""
 
 
 def test_binding_rejects_host_tensors():

@@ -98,12 +98,14 @@ def test_beam_config(name):
 # ------------------------------------------------------- envelope sweeps ----
 
 SWEEP_H = [256, 768, 1280, 2048, 3840, 4096, 7168, 8192]
-# One top-k per kernel variant: run-time top-k sized for 2 slots (1, 2), 4
-# slots (3, 4) and 8 slots (6, 7), compile-time 8 and 16, and run-time top-k
-# above 8 in one batch (9, 12) or several (24, 32).  With the hidden sizes
-# above this also covers one, two, four and eight vectors per thread and the
-# half-idle last wave of odd hidden / 256.
-SWEEP_K = [1, 2, 3, 4, 6, 7, 8, 9, 12, 16, 24, 32]
+# Each kernel variant at a full and a partly used slot count: run-time top-k
+# sized for 2 slots (1, 2), 4 (3, 4), 8 (6, 7), 12 (9, 12), 16 (13), 24
+# (17, 24) and 32 (25, 32), and compile-time 8 and 16.  Above 8 slots the
+# rows arrive in one batch or through the rolling window, depending on the
+# vectors per thread.  With the hidden sizes above this also covers one,
+# two, four and eight vectors per thread and the half-idle last wave of odd
+# hidden / 256.
+SWEEP_K = [1, 2, 3, 4, 6, 7, 8, 9, 12, 13, 16, 17, 24, 25, 32]
 
 
 @pytest.mark.parametrize("hidden", SWEEP_H)
@@ -560,6 +562,115 @@ def test_token_major_offsets_beyond_4_gib_sampled():
     want = oracle.beam_moe_finalize(host_bits(e[pick_t]), w[pick_t].cpu().numpy(), len(pick),
                                     1.5, host_bits(pw), 1e-6)
     assert_within_ulp(got, want, 1, NORM_MIN_EXACT, "sampled token-major rows past 4 GiB")
+    del e, out
+    torch.cuda.empty_cache()
+
+
+def test_negative_zero_passes_through_direct_rows():
+    """Rows read directly (the standalone norm and the residual consumer)
+    keep -0: the sum starts from -0, so fma(1, -0, -0) stays -0 where a +0
+    start would turn it into +0.  Elements whose oracle value is a zero must
+    match it bit for bit, sign included (the ulp comparison counts +0 and -0
+    as equal); the rest within 1 ulp."""
+    rng = np.random.Generator(np.random.PCG64(97))
+    T, H = 9, 1024
+    x = wl.normal_bf16(rng, (T, H))
+    x[:, ::5] = 0x8000                               # -0 in a fifth of the columns
+    x[:, 1::7] = 0x0000
+    res = np.full((T, H), 0x8000, np.uint16)         # residual -0 everywhere
+    res[:, 3::4] = wl.normal_bf16(rng, (T, len(range(3, H, 4))))
+    nw = wl.normal_bf16(rng, (H,), mean=0.0, std=1.0)  # mixed signs: -0 * g < 0 gives +0
+    xd, resd, nwd = dev_bf16(x), dev_bf16(res), dev_bf16(nw)
+
+    def check(got, want, what):
+        zero = (want & 0x7FFF) == 0
+        assert zero.any()
+        assert np.array_equal(got[zero], want[zero]), f"{what}: signed zeros differ"
+        assert_within_ulp(got, want, 1, NORM_MIN_EXACT, what)
+
+    for wbn in (False, True):
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        mf.mf_rmsnorm(xd, nwd, out, eps=1e-6, gain_center=0.0, weight_before_norm=wbn)
+        sync()
+        want = oracle.rmsnorm(x, nw, eps=1e-6, gain_center=0.0, weight_before_norm=wbn)
+        check(host_bits(out), want, f"mf_rmsnorm wbn={wbn}")
+    h, n = mf.beam_norm_residual_norm(xd, resd, None, None, nwd, 1e-6, None)
+    sync()
+    wh, wn = oracle.beam_norm_residual_norm(x, res, None, None, nw, 1e-6, None)
+    assert np.array_equal(host_bits(h), wh), "hidden = x + residual differs (signed zeros)"
+    check(host_bits(n), wn, "normalized")
+
+
+def _split_sample(T, boundary, seed):
+    """Tokens to compare on a call split into launches: both sides of the
+    first launch boundary, the first and last tokens, and a random spread."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    near = np.arange(boundary - 64, boundary + 64)
+    return np.unique(np.concatenate([np.arange(64), near, np.arange(T - 64, T),
+                                     rng.integers(0, T, 1000)]))
+
+
+@pytest.mark.parametrize("H,K,team", [(256, 1, 64), (4096, 8, 512)])
+def test_index_map_split_into_launches_sampled(H, K, team):
+    """A token count whose grid exceeds the 2^31 work-items one launch may
+    span (teams of `team` threads): the call runs as several launches, each
+    from its own first token.  Tokens on both sides of the first launch
+    boundary, at both ends and spread over the range are compared with the
+    oracle (hidden 256 without a norm: bit-exact; hidden 4096 with the norm:
+    within 1 ulp)."""
+    per_launch = 2 ** 31 // team
+    T, R = per_launch + 3000, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(90 + K)
+    rows = torch.randn((R, H), generator=gen, device="cuda").to(torch.bfloat16)
+    idx = torch.randint(-R // 64, R, (T, K), generator=gen, device="cuda", dtype=torch.int32)
+    w = torch.softmax(torch.randn((T, K), generator=gen, device="cuda"), dim=1)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    pick = _split_sample(T, per_launch, 91 + K)
+    pick_t = torch.from_numpy(pick).cuda()
+    if K == 1:
+        mf.moe_finalize(rows, w, idx, out)
+        sync()
+        want = oracle.moe_finalize(host_bits(rows), w[pick_t].cpu().numpy(),
+                                   idx[pick_t].cpu().numpy(), H)
+        assert_bits_equal(host_bits(out[pick_t]), want, "tokens across the launch split")
+    else:
+        nw = (0.1 * torch.randn(H, generator=gen, device="cuda")).to(torch.bfloat16)
+        mf.moe_finalize_rmsnorm(rows, w, idx, nw, out, eps=1e-6, gain_center=1.0,
+                                weight_before_norm=False)
+        sync()
+        want = oracle.moe_finalize_rmsnorm(host_bits(rows), w[pick_t].cpu().numpy(),
+                                           idx[pick_t].cpu().numpy(), host_bits(nw), eps=1e-6,
+                                           gain_center=1.0, weight_before_norm=False)
+        assert_within_ulp(host_bits(out[pick_t]), want, 1, NORM_MIN_EXACT,
+                          "tokens across the launch split")
+    del out, idx, w
+    torch.cuda.empty_cache()
+
+
+def test_token_major_split_into_launches_sampled():
+    """Token-major rows at hidden 256 (teams of 64) for 2^25 + 3000 live
+    tokens (17 GB of rows): two launches.  Sampled tokens around the
+    boundary and across the range are compared with the oracle bit for bit
+    (no norm, routed_scale 1.25)."""
+    per_launch = 2 ** 31 // 64
+    C = per_launch + 3000
+    H = 256
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(95)
+    e = torch.empty((C, 1, H), dtype=torch.bfloat16, device="cuda")
+    for s in range(0, C, 1 << 24):
+        n = min(1 << 24, C - s)
+        e[s:s + n] = torch.randn((n, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
+    w = torch.rand((C, 1), generator=gen, device="cuda") + 0.5
+    out = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
+    mf.beam_moe_finalize(e, w, out, 1.25)
+    sync()
+    pick = _split_sample(C, per_launch, 96)
+    pick_t = torch.from_numpy(pick).cuda()
+    want = oracle.beam_moe_finalize(host_bits(e[pick_t]), w[pick_t].cpu().numpy(), len(pick),
+                                    1.25)
+    assert_bits_equal(host_bits(out[pick_t]), want, "token-major tokens across the launch split")
     del e, out
     torch.cuda.empty_cache()
 
