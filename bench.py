@@ -65,6 +65,9 @@ def parse_args():
     p.add_argument("--config", default="prefill", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the memory-system probes and the per-dispatch pass "
+                        "(profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle sample")
     p.add_argument("--graph", action="store_true",
@@ -465,7 +468,7 @@ def copy_probe(torch, mib: int = 1024, reps: int = 10) -> float:
 
 # ------------------------------------------------- memory-system ceilings --
 
-PROBE_BLOCKS = (1024, 2048, 4096, 8192)
+PROBE_BLOCKS = (1024, 2048, 4096, 8192)   # grid-stride probes: workgroups of 256
 PROBE_POLICIES = (0, 2, 16)        # store cache policy: default, nt, sc1
 PROBE_BYTES = 1 << 30              # per probe: far beyond the 256 MB Infinity Cache
 
@@ -482,9 +485,14 @@ def load_probes():
     so.mf_probe_read.argtypes = [vp, i64, vp, i32, i32, vp]
     so.mf_probe_write.argtypes = [vp, i64, i32, i32, i32, vp]
     so.mf_probe_mixed.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
-    for f in (so.mf_probe_read, so.mf_probe_write, so.mf_probe_mixed):
+    so.mf_probe_rows.argtypes = [i32, i32, i32, vp, vp, vp, i64, i32, i64, vp]
+    for f in (so.mf_probe_read, so.mf_probe_write, so.mf_probe_mixed, so.mf_probe_rows):
         f.restype = i32
     return so
+
+
+PROBE_TEAMS = (256, 512)
+PROBE_RESIDENT = (0, 2, 4, 8)      # workgroups per CU the row probes allow (0: no cap)
 
 
 def probe_ratio(read_write_ratio: float) -> int:
@@ -493,11 +501,16 @@ def probe_ratio(read_write_ratio: float) -> int:
 
 
 def memory_ceilings(torch, read_write_ratio: float, reps: int = 10) -> dict:
-    """Best GB/s of three streaming probes in this run, over launch shapes
-    (PROBE_BLOCKS workgroups of 256 threads) and store cache policies: read
-    only, write only, and reads and writes mixed in the workload's own
-    proportion (rounded to 4, 8 or 16 reads per write), all coalesced.  The
-    mixed figure is the practical ceiling for the kernel's traffic."""
+    """Best GB/s of streaming probes in this run, for three traffic mixes:
+    read only, write only, and reads and writes in the workload's own
+    proportion (rounded to 4, 8 or 16 reads per write).  Two probe shapes
+    are tried over launch shapes, residency caps and store cache policies:
+    grid-stride loops (PROBE_BLOCKS workgroups of 256 threads), and the
+    finalize's own shape of work without its arithmetic (one workgroup per
+    token reading `ratio` contiguous rows of team x 16 bytes, all in flight,
+    and writing one row; teams PROBE_TEAMS, PROBE_RESIDENT workgroups per
+    CU).  The mixed figure is the practical ceiling for the kernel's traffic:
+    the same mix with every access contiguous."""
     so = load_probes()
     stream = torch.cuda.current_stream().cuda_stream
     ratio = probe_ratio(read_write_ratio)
@@ -506,40 +519,65 @@ def memory_ceilings(torch, read_write_ratio: float, reps: int = 10) -> dict:
     src.random_(0, 255)
     dst = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
     flag = torch.zeros(64, dtype=torch.int32, device="cuda")
+    lds_cu = getattr(torch.cuda.get_device_properties(0), "shared_memory_per_multiprocessor",
+                     160 * 1024)
+
+    def rate(go, nbytes):
+        rc = go()
+        assert rc == 0, f"probe launch failed ({rc})"
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            go()
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+
+    best = {"read": (0.0, ""), "write": (0.0, ""), "mixed": (0.0, "")}
+
+    def keep(mode, gbps, how):
+        if gbps > best[mode][0]:
+            best[mode] = (gbps, how)
+
     out16 = n16 // ratio
-
-    def timed(launch, nbytes):
-        best = 0.0
-        for blocks in PROBE_BLOCKS:
-            for extra in launch["variants"]:
-                def go():
-                    rc = launch["fn"](blocks, extra)
-                    assert rc == 0, f"probe launch failed ({rc})"
-                go()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(reps):
-                    go()
-                e1.record()
-                torch.cuda.synchronize()
-                best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9)
-        return best
-
-    read = timed({"fn": lambda b, _: so.mf_probe_read(src.data_ptr(), n16, flag.data_ptr(), b,
-                                                      256, stream), "variants": (None,)},
-                 PROBE_BYTES)
-    write = timed({"fn": lambda b, pol: so.mf_probe_write(dst.data_ptr(), n16, pol, b, 256,
-                                                          stream),
-                   "variants": PROBE_POLICIES}, PROBE_BYTES)
-    mixed = timed({"fn": lambda b, pol: so.mf_probe_mixed(src.data_ptr(), dst.data_ptr(),
-                                                          out16, ratio, pol, b, 256, stream),
-                   "variants": PROBE_POLICIES}, out16 * 16 * (ratio + 1))
+    for blocks in PROBE_BLOCKS:
+        keep("read", rate(lambda: so.mf_probe_read(src.data_ptr(), n16, flag.data_ptr(), blocks,
+                                                   256, stream), PROBE_BYTES),
+             f"grid-stride, {blocks} x 256")
+        for pol in PROBE_POLICIES:
+            keep("write", rate(lambda: so.mf_probe_write(dst.data_ptr(), n16, pol, blocks, 256,
+                                                         stream), PROBE_BYTES),
+                 f"grid-stride, {blocks} x 256, store policy {pol}")
+            keep("mixed", rate(lambda: so.mf_probe_mixed(src.data_ptr(), dst.data_ptr(), out16,
+                                                         ratio, pol, blocks, 256, stream),
+                               out16 * 16 * (ratio + 1)),
+                 f"grid-stride, {blocks} x 256, store policy {pol}")
+    for team in PROBE_TEAMS:
+        tokens = PROBE_BYTES // (ratio * team * 16)
+        for resident in PROBE_RESIDENT:
+            lds = lds_cu // resident - 1024 if resident else 0
+            where = f"one token per workgroup of {team}, {resident or 'uncapped'} per CU"
+            keep("read", rate(lambda: so.mf_probe_rows(0, ratio, 0, src.data_ptr(), None,
+                                                       flag.data_ptr(), tokens, team, lds,
+                                                       stream), tokens * ratio * team * 16),
+                 where)
+            for pol in PROBE_POLICIES:
+                keep("write", rate(lambda: so.mf_probe_rows(1, ratio, pol, None, dst.data_ptr(),
+                                                            None, tokens, team, lds, stream),
+                                   tokens * ratio * team * 16), f"{where}, store policy {pol}")
+                keep("mixed", rate(lambda: so.mf_probe_rows(2, ratio, pol, src.data_ptr(),
+                                                            dst.data_ptr(), None, tokens, team,
+                                                            lds, stream),
+                                   tokens * (ratio + 1) * team * 16),
+                     f"{where}, store policy {pol}")
     del src, dst, flag
     torch.cuda.empty_cache()
-    return {"read_only_GBps": read, "write_only_GBps": write, "mixed_GBps": mixed,
-            "mixed_reads_per_write": ratio, "bytes_per_probe": PROBE_BYTES,
-            "note": "best of launch shapes and store cache policies, same run"}
+    return {"read_only_GBps": best["read"][0], "write_only_GBps": best["write"][0],
+            "mixed_GBps": best["mixed"][0], "mixed_reads_per_write": ratio,
+            "best_shapes": {k: v[1] for k, v in best.items()},
+            "bytes_per_probe": PROBE_BYTES,
+            "note": "best of probe shapes, residency caps and store cache policies, same run"}
 
 
 def dispatch_stats(torch, step, first: int, steps: int) -> dict:
@@ -574,7 +612,9 @@ def envelope(torch, mf, wl, steps: int, warmup: int, shapes: str = "",
     token count gives about 256 MiB of gathered rows per launch, and steps
     rotate over copies totalling at least 1.5 GiB, as in the main bench.  A
     cell's time is the median of ENVELOPE_SPANS spans of steps / ENVELOPE_SPANS
-    back-to-back launches."""
+    back-to-back launches.  The rows are drawn in BF16 in place and every
+    cell's buffers are released before the next, so no cell runs in memory
+    left fragmented by a larger one's temporaries."""
     import numpy as np
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
@@ -595,7 +635,8 @@ def envelope(torch, mf, wl, steps: int, warmup: int, shapes: str = "",
             rng = np.random.Generator(np.random.PCG64(1000 * H + K))
             w = torch.from_numpy(wl.softmax_rows(rng.standard_normal((T, K)) * 2.0)).to(dev)
             nw = (torch.randn(H, generator=gen, device=dev) * 0.1).to(torch.bfloat16)
-            rows = torch.randn((T * K, H), generator=gen, device=dev).to(torch.bfloat16)
+            rows = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+            rows.normal_(generator=gen)
             per_set = rows.numel() * 2 + T * H * 2
             sets = max(2, math.ceil(ROTATE_MIN_BYTES / per_set))
             rs = [rows] + [rows.clone() for _ in range(sets - 1)]
@@ -617,19 +658,19 @@ def envelope(torch, mf, wl, steps: int, warmup: int, shapes: str = "",
             for i in range(warmup):
                 step(i)
             torch.cuda.synchronize()
-            # The median of ENVELOPE_SPANS spans of back-to-back launches, so
-            # one disturbed span does not decide a cell.
+            # ENVELOPE_SPANS spans of back-to-back launches, the events of
+            # consecutive spans recorded between launches with no wait in
+            # between (the GPU never idles, as in the headline's single
+            # span); the median span, so one disturbed span does not decide.
             per = max(1, steps // ENVELOPE_SPANS)
-            spans = []
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(ENVELOPE_SPANS + 1)]
+            ev[0].record()
             for r in range(ENVELOPE_SPANS):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
                 for i in range(per):
                     step(warmup + r * per + i)
-                e1.record()
-                torch.cuda.synchronize()
-                spans.append(e0.elapsed_time(e1) * 1e3 / per)
+                ev[r + 1].record()
+            torch.cuda.synchronize()
+            spans = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / per for r in range(ENVELOPE_SPANS)]
             us = sorted(spans)[len(spans) // 2]
             gbps = nbytes / us / 1e3
             results.append({"layout": layout, "hidden": H, "top_k": K, "tokens": T,
@@ -739,15 +780,18 @@ def main():
     torch.cuda.synchronize()
     hot_us = hot_start.elapsed_time(hot_end) * 1e3 / K
     traffic = stored_traffic(args.config)
-    dispatch = dispatch_stats(torch, bench.step, args.warmup + K, K)
-    dispatch["span_mean_us"] = kern_avg_s * 1e6
-    dispatch["note"] = ("event pair around each launch in a separate pass; the gaps the "
-                        "events add make these read high by about mean_us - span_mean_us")
-    ceil = memory_ceilings(torch, bench.read_write_ratio())
-    log(f"bench: kernel avg {kern_avg_s * 1e6:.2f} us, {achieved:.0f} GB/s; per dispatch "
-        f"median {dispatch['median_us']:.2f} us, min {dispatch['min_us']:.2f} us; ceilings "
-        f"read {ceil['read_only_GBps']:.0f}, write {ceil['write_only_GBps']:.0f}, "
-        f"{ceil['mixed_reads_per_write']}:1 mix {ceil['mixed_GBps']:.0f} GB/s; "
+    dispatch, ceil = None, None
+    if not args.no_probes:
+        dispatch = dispatch_stats(torch, bench.step, args.warmup + K, K)
+        dispatch["span_mean_us"] = kern_avg_s * 1e6
+        dispatch["note"] = ("event pair around each launch in a separate pass; the gaps the "
+                            "events add make these read high by about mean_us - span_mean_us")
+        ceil = memory_ceilings(torch, bench.read_write_ratio())
+        log(f"bench: per dispatch median {dispatch['median_us']:.2f} us, min "
+            f"{dispatch['min_us']:.2f} us; ceilings read {ceil['read_only_GBps']:.0f}, write "
+            f"{ceil['write_only_GBps']:.0f}, {ceil['mixed_reads_per_write']}:1 mix "
+            f"{ceil['mixed_GBps']:.0f} GB/s")
+    log(f"bench: kernel avg {kern_avg_s * 1e6:.2f} us, {achieved:.0f} GB/s; "
         f"wall {wall * 1e3 / K:.3f} ms/step")
 
     unfused = None
@@ -794,7 +838,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "kernel_avg_us": kern_avg_s * 1e6,
-                     "frac_of_practical_ceiling": achieved / ceil["mixed_GBps"],
+                     "frac_of_practical_ceiling": achieved / ceil["mixed_GBps"] if ceil else None,
                      "practical_ceiling": ceil, "dispatch": dispatch},
         "cpu_baseline": cpu,
         "unfused_baseline": unfused,

@@ -14,6 +14,14 @@
 //
 // Each thread moves 16-byte vectors in a grid-stride loop; `blocks` and
 // `threads` set the launch so the caller can take the best of several.
+//
+//   mf_probe_rows    the finalize's own shape of work without its arithmetic:
+//                    one workgroup per "token" reads `ratio` contiguous rows
+//                    of team x 16 bytes (all in flight at once) and writes
+//                    one row, or only reads, or only writes `ratio` rows;
+//                    dynamic LDS caps the workgroups resident on a CU, as
+//                    the finalize launcher does
+//
 // The arithmetic is integer adds and XORs, negligible against the traffic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -77,6 +85,74 @@ __global__ void probe_mixed(const u32x4 *__restrict__ in, u32x4 *__restrict__ ou
         for (int k = 1; k < R; ++k)
             s += v[k];
         __builtin_amdgcn_raw_buffer_store_b128(s, r, (uint32_t)(i * 16), 0, POL);
+    }
+}
+
+// One workgroup per token: MODE 0 reads R rows, 1 writes R rows, 2 reads R
+// rows and writes one.  A row is blockDim.x 16-byte vectors.
+template <int R, int MODE, int POL>
+__global__ void __launch_bounds__(1024)
+probe_rows(const u32x4 *__restrict__ in, u32x4 *__restrict__ out, uint32_t out_bytes,
+           uint32_t *flag)
+{
+    const int64_t row = blockDim.x;
+    const int64_t tok = blockIdx.x;
+    const int j = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t r = out_resource(out, out_bytes);
+    if constexpr (MODE == 1) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const uint32_t v = (uint32_t)(tok * R + k) ^ (uint32_t)j;
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){v, v, v, v}, r,
+                                                   (uint32_t)(((tok * R + k) * row + j) * 16),
+                                                   0, POL);
+        }
+    } else {
+        const u32x4 *src = in + tok * R * row + j;
+        u32x4 v[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            v[k] = __builtin_nontemporal_load(src + k * row);
+        u32x4 sum = v[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k)
+            sum += v[k];
+        if constexpr (MODE == 0) {
+            if (sum.x == 0x9E3779B9u && sum.y == 0x7F4A7C15u && sum.z == 0x94D049BBu &&
+                sum.w == 0x2545F491u)
+                flag[0] = 1u + threadIdx.x;   // never in practice; keeps the loads alive
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b128(sum, r, (uint32_t)((tok * row + j) * 16), 0,
+                                                   POL);
+        }
+    }
+}
+
+template <int R, int MODE>
+hipError_t launch_rows(int policy, const void *in, void *out, uint32_t out_bytes, void *flag,
+                       dim3 g, dim3 b, size_t lds, hipStream_t s)
+{
+    const u32x4 *i = (const u32x4 *)in;
+    u32x4 *o = (u32x4 *)out;
+    uint32_t *f = (uint32_t *)flag;
+    switch (policy) {
+    case 0: hipLaunchKernelGGL((probe_rows<R, MODE, 0>), g, b, lds, s, i, o, out_bytes, f); break;
+    case 2: hipLaunchKernelGGL((probe_rows<R, MODE, 2>), g, b, lds, s, i, o, out_bytes, f); break;
+    case 16: hipLaunchKernelGGL((probe_rows<R, MODE, 16>), g, b, lds, s, i, o, out_bytes, f); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_rows_mode(int mode, int policy, const void *in, void *out, uint32_t out_bytes,
+                            void *flag, dim3 g, dim3 b, size_t lds, hipStream_t s)
+{
+    switch (mode) {
+    case 0: return launch_rows<R, 0>(policy, in, out, out_bytes, flag, g, b, lds, s);
+    case 1: return launch_rows<R, 1>(policy, in, out, out_bytes, flag, g, b, lds, s);
+    case 2: return launch_rows<R, 2>(policy, in, out, out_bytes, flag, g, b, lds, s);
+    default: return hipErrorInvalidValue;
     }
 }
 
@@ -160,6 +236,34 @@ __attribute__((visibility("default"))) int mf_probe_mixed(const void *in, void *
     case 4: return (int)launch_mixed_pol<4>(policy, in, out, n16_out, g, b, s);
     case 8: return (int)launch_mixed_pol<8>(policy, in, out, n16_out, g, b, s);
     case 16: return (int)launch_mixed_pol<16>(policy, in, out, n16_out, g, b, s);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+// tokens workgroups of `threads` threads; mode 0 reads tokens x ratio rows
+// of `in`, 1 writes tokens x ratio rows of `out`, 2 reads tokens x ratio rows
+// and writes tokens rows.  A row is threads x 16 bytes; the output stays
+// below 4 GiB.  lds_bytes of dynamic LDS per workgroup (0: none).
+__attribute__((visibility("default"))) int mf_probe_rows(int mode, int ratio, int policy,
+                                                          const void *in, void *out, void *flag,
+                                                          int64_t tokens, int threads,
+                                                          int64_t lds_bytes, void *stream)
+{
+    if (tokens <= 0 || tokens > INT32_MAX || threads < 64 || threads > 1024 ||
+        threads % 64 != 0 || lds_bytes < 0 || lds_bytes > 160 * 1024 || mode < 0 || mode > 2)
+        return (int)hipErrorInvalidValue;
+    if ((mode != 1 && !in) || (mode != 0 && !out) || (mode == 0 && !flag))
+        return (int)hipErrorInvalidValue;
+    const int64_t out_rows = mode == 1 ? tokens * ratio : mode == 2 ? tokens : 1;
+    const int64_t out_bytes = out_rows * threads * 16;
+    if (out_bytes >= (int64_t(1) << 32))
+        return (int)hipErrorInvalidValue;
+    const dim3 g((unsigned)tokens), b(threads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (ratio) {
+    case 4: return (int)launch_rows_mode<4>(mode, policy, in, out, (uint32_t)out_bytes, flag, g, b, (size_t)lds_bytes, s);
+    case 8: return (int)launch_rows_mode<8>(mode, policy, in, out, (uint32_t)out_bytes, flag, g, b, (size_t)lds_bytes, s);
+    case 16: return (int)launch_rows_mode<16>(mode, policy, in, out, (uint32_t)out_bytes, flag, g, b, (size_t)lds_bytes, s);
     default: return (int)hipErrorInvalidValue;
     }
 }

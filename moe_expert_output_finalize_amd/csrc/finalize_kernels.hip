@@ -170,225 +170,19 @@ __device__ __forceinline__ float lane_value(float v, int l)
 
 // ------------------------------------------------------------ kernel -----
 
-// One workgroup finalizes token a.token_base + blockIdx.x.
-//   L      where slot rows come from (index map, token major, one row per token)
-//   W_BF16 weights are BF16 (else FP32)
-//   EPI    what follows the FP32 routed sum
-//   KC     top_k when known at compile time (> 0), else minus the largest
-//          top-k the kernel serves (a.top_k is read at run time)
-//   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
-//
-// Slots whose rows all fit in flight (slots_in_flight) arrive as one batch:
-// every valid slot's row vectors are issued, then the FMAs run.  More slots
-// than that stream through a rolling window of W slots: the rows of slot
-// s + W are issued as soon as slot s has been reduced, so a token's loads
-// never drain between groups of slots.  The window's code is straight-line:
-// its loads go through buffer resources, and an invalid slot, or one past a
-// run-time top-k, gets an empty resource whose loads return zeros without
-// touching memory, and weight 0.  Every load is then unconditional, the
-// compiler waits for exactly the slot being reduced, and a scheduling
-// barrier per slot keeps each slot's loads W slots ahead of its FMAs instead
-// of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
-// starts at +0 never becomes -0.
-template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
-__global__ void __launch_bounds__(max_team(VPT))
-finalize_kernel(const FinalizeArgs a)
+// What follows a token's FP32 routed sum `acc`: the epilogue EPI and the
+// stores of token t's output row(s).  gv holds the norm weight (or post
+// weight) vectors and rv the token's residual vectors, as the epilogue needs.
+// All threads of the workgroup call it (the norms contain a barrier).
+template <Epilogue EPI, int VPT, bool EXACT>
+__device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (&gv)[VPT],
+                                             const u32x4 (&rv)[VPT], const FinalizeArgs &a,
+                                             int64_t t, int lane, int team, int nv)
 {
-    constexpr bool kIdx = L == Layout::kIndexMap;
-    constexpr int KB = slots_in_flight(kIdx, KC, VPT);
-    constexpr bool kRoll = rolling(kIdx, KC, VPT);
-    constexpr int kSlotsMax = KC > 0 ? KC : -KC;
-    static_assert(KB >= 1 && (kRoll || KC <= 0 || KC % KB == 0), "batches divide top-k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
     constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
                                    EPI == Epilogue::kResidualNorm;
-    const int top_k = KC > 0 ? KC : a.top_k;
-    const int team = blockDim.x;
-    const int lane = threadIdx.x;
-    const int nv = a.hidden >> 3;
-    const int64_t t = a.token_base + blockIdx.x;
-    const int64_t tk = t * top_k;
-
-    // The norm weight is shared by every token and stays cache resident;
-    // fetch it first so its latency hides under the gather.
-    u32x4 gv[VPT];
-    if constexpr (kNorm || EPI == Epilogue::kResidualNorm) {
-        const bool have = (EPI != Epilogue::kBeamNorm && EPI != Epilogue::kResidualNorm) ||
-                          a.gain != nullptr;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;
-            gv[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (have && (EXACT || j < nv))
-                gv[i] = reinterpret_cast<const u32x4 *>(a.gain)[j];
-        }
-    }
-
-    // The residual row of this token, for the residual epilogue.
-    u32x4 rv[VPT];
-    if constexpr (EPI == Epilogue::kResidualNorm) {
-        const u32x4 *rr = reinterpret_cast<const u32x4 *>(a.residual + t * (int64_t)a.hidden);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;
-            rv[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (EXACT || j < nv)
-                rv[i] = load_row_vec(rr + j);
-        }
-    }
-
-    // A direct row starts from -0, so that fma(1, x, -0) == x for every x,
-    // -0 included; a routed sum starts from +0.
-    constexpr float kAcc0 = L == Layout::kDirect ? -0.0f : 0.0f;
-    float acc[VPT][8];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[i][e] = kAcc0;
-
-    if constexpr (kRoll) {
-        constexpr int W = KB;
-        // Slot metadata in VGPRs: lane l of every wave holds slot l's index
-        // and weight (lanes past top-k an invalid index and weight 0), read
-        // back as scalars per slot.  The loads are unconditional: lanes past
-        // top-k re-read the last slot.
-        const int wl = lane & (kWave - 1);
-        const int64_t ms = tk + (wl < top_k ? wl : top_k - 1);
-        int32_t m_idx = -1;
-        if constexpr (kIdx)
-            m_idx = a.idx[ms];
-        float m_w = load_weight<W_BF16>(a.weights, ms);
-        if (wl >= top_k) {
-            m_idx = -1;
-            m_w = 0.0f;
-        }
-
-        u32x4 v[W][VPT];
-        float wt[W];
-        // The row address is computed whether or not the slot is valid (an
-        // empty resource never dereferences it): a select between it and a
-        // constant would be turned into a branch, and branches between the
-        // slots would let the compiler sink each slot's FMAs past the loads
-        // that follow them.
-        const uint64_t rows = reinterpret_cast<uintptr_t>(a.rows);
-        auto issue = [&](int s) {
-            const int b = s % W;
-            const float w = lane_value(m_w, s);
-            bool ok;
-            int64_t off;   // elements
-            if constexpr (kIdx) {
-                const int32_t i = lane_value(m_idx, s);
-                ok = i >= 0 && (int64_t)i < a.num_rows;
-                off = (int64_t)i * a.row_stride;
-            } else {
-                ok = KC > 0 || s < top_k;
-                off = (tk + s) * (int64_t)a.hidden;
-            }
-            wt[b] = ok ? w : 0.0f;
-            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-                reinterpret_cast<void *>(rows + 2 * (uint64_t)off), 0, ok ? nv * 16 : 0,
-                kRawBufferWord3);
-#pragma unroll
-            for (int i = 0; i < VPT; ++i)   // vectors past the row read as zeros
-                v[b][i] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + i * team) * 16, 0,
-                                                                MF_ROW_LOAD_POLICY);
-        };
-#pragma unroll
-        for (int s = 0; s < W; ++s)
-            issue(s);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < kSlotsMax; ++s) {
-            const int b = s % W;
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[i][e] = __builtin_fmaf(wt[b], elem(v[b][i], e), acc[i][e]);
-                // An empty statement that reads and writes the sums keeps this
-                // slot's FMAs here: otherwise instruction selection may place
-                // every slot's FMAs after the last barrier, with all 32 slots'
-                // rows held in registers.
-                asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]),
-                             "+v"(acc[i][3]), "+v"(acc[i][4]), "+v"(acc[i][5]),
-                             "+v"(acc[i][6]), "+v"(acc[i][7]));
-            }
-            if (s + W < kSlotsMax)
-                issue(s + W);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        // Batches of KB slots (one batch when every slot fits): uniform
-        // per-slot data first (scalar loads, one wait), then every valid
-        // slot's row vectors, then the FMAs in ascending slot order.  The
-        // batches are unrolled up to the slots the kernel serves, with a
-        // uniform exit past a run-time top-k.
-#pragma unroll
-        for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
-            if (KC < 0 && k0 >= top_k)
-                break;
-            int64_t row_off[KB];   // elements
-            bool ok[KB];
-            float w[KB];
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                // Slots past a run-time top-k re-read the token's last slot
-                // (always in bounds) and are masked: the metadata loads stay
-                // unconditional, so they issue together behind one wait.
-                const int k = k0 + b;
-                const bool live = KC > 0 || k < top_k;
-                const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
-                if constexpr (kIdx) {
-                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
-                    const int32_t i = a.idx[tk + kk];
-                    ok[b] = live && i >= 0 && (int64_t)i < a.num_rows;
-                    row_off[b] = (int64_t)i * a.row_stride;
-                } else if constexpr (L == Layout::kTokenMajor) {
-                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
-                    ok[b] = live;
-                    row_off[b] = (tk + kk) * (int64_t)a.hidden;
-                } else {   // kDirect
-                    w[b] = 1.0f;
-                    ok[b] = live;
-                    row_off[b] = t * a.row_stride;
-                }
-            }
-            u32x4 v[KB][VPT];
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                if (ok[b]) {
-                    const u32x4 *r = reinterpret_cast<const u32x4 *>(a.rows + row_off[b]);
-#pragma unroll
-                    for (int i = 0; i < VPT; ++i) {
-                        const int j = lane + i * team;
-                        if (EXACT || j < nv)
-                            v[b][i] = load_row_vec(r + j);
-                        else
-                            v[b][i] = (u32x4){0u, 0u, 0u, 0u};
-                    }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                if (ok[b]) {
-#pragma unroll
-                    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
-                }
-            }
-            // Every gather of this batch has been consumed.  Saying so keeps
-            // the compiler, which cannot pair each conditional load with its
-            // conditional use, from waiting before each gather of the next
-            // batch.
-            if constexpr (kSlotsMax > KB)
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        }
-    }
-
     const __amdgpu_buffer_rsrc_t out_row =
         row_resource(a.out + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
     auto store = [&](int i, const u32x4 &o) {
@@ -555,6 +349,226 @@ finalize_kernel(const FinalizeArgs a)
             store(i, o);
         }
     }
+}
+
+// One workgroup finalizes token a.token_base + blockIdx.x.
+//   L      where slot rows come from (index map, token major, one row per token)
+//   W_BF16 weights are BF16 (else FP32)
+//   EPI    what follows the FP32 routed sum
+//   KC     top_k when known at compile time (> 0), else minus the largest
+//          top-k the kernel serves (a.top_k is read at run time)
+//   VPT    16-byte vectors per thread; EXACT: hidden / 8 == blockDim.x * VPT
+//
+// Slots whose rows all fit in flight (slots_in_flight) arrive as one batch:
+// every valid slot's row vectors are issued, then the FMAs run.  More slots
+// than that stream through a rolling window of W slots: the rows of slot
+// s + W are issued as soon as slot s has been reduced, so a token's loads
+// never drain between groups of slots.  The window's code is straight-line:
+// its loads go through buffer resources, and an invalid slot, or one past a
+// run-time top-k, gets an empty resource whose loads return zeros without
+// touching memory, and weight 0.  Every load is then unconditional, the
+// compiler waits for exactly the slot being reduced, and a scheduling
+// barrier per slot keeps each slot's loads W slots ahead of its FMAs instead
+// of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
+// starts at +0 never becomes -0.
+template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
+__global__ void __launch_bounds__(max_team(VPT))
+finalize_kernel(const FinalizeArgs a)
+{
+    constexpr bool kIdx = L == Layout::kIndexMap;
+    constexpr int KB = slots_in_flight(kIdx, KC, VPT);
+    constexpr bool kRoll = rolling(kIdx, KC, VPT);
+    constexpr int kSlotsMax = KC > 0 ? KC : -KC;
+    static_assert(KB >= 1 && (kRoll || KC <= 0 || KC % KB == 0), "batches divide top-k");
+    constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
+                           EPI == Epilogue::kBeamNorm;
+    const int top_k = KC > 0 ? KC : a.top_k;
+    const int team = blockDim.x;
+    const int lane = threadIdx.x;
+    const int nv = a.hidden >> 3;
+    const int64_t t = a.token_base + blockIdx.x;
+    const int64_t tk = t * top_k;
+
+    // The norm weight is shared by every token and stays cache resident;
+    // fetch it first so its latency hides under the gather.
+    u32x4 gv[VPT];
+    if constexpr (kNorm || EPI == Epilogue::kResidualNorm) {
+        const bool have = (EPI != Epilogue::kBeamNorm && EPI != Epilogue::kResidualNorm) ||
+                          a.gain != nullptr;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int j = lane + i * team;
+            gv[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (have && (EXACT || j < nv))
+                gv[i] = reinterpret_cast<const u32x4 *>(a.gain)[j];
+        }
+    }
+
+    // The residual row of this token, for the residual epilogue.
+    u32x4 rv[VPT];
+    if constexpr (EPI == Epilogue::kResidualNorm) {
+        const u32x4 *rr = reinterpret_cast<const u32x4 *>(a.residual + t * (int64_t)a.hidden);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int j = lane + i * team;
+            rv[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (EXACT || j < nv)
+                rv[i] = load_row_vec(rr + j);
+        }
+    }
+
+    // A direct row starts from -0, so that fma(1, x, -0) == x for every x,
+    // -0 included; a routed sum starts from +0.
+    constexpr float kAcc0 = L == Layout::kDirect ? -0.0f : 0.0f;
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[i][e] = kAcc0;
+
+    if constexpr (kRoll) {
+        constexpr int W = KB < kSlotsMax ? KB : kSlotsMax;
+        // Slot metadata in VGPRs: lane l of every wave holds slot l's index
+        // and weight (lanes past top-k an invalid index and weight 0), read
+        // back as scalars per slot.  The loads are unconditional: lanes past
+        // top-k re-read the last slot.
+        const int wl = lane & (kWave - 1);
+        const int64_t ms = tk + (wl < top_k ? wl : top_k - 1);
+        int32_t m_idx = -1;
+        if constexpr (kIdx)
+            m_idx = a.idx[ms];
+        float m_w = load_weight<W_BF16>(a.weights, ms);
+        if (wl >= top_k) {
+            m_idx = -1;
+            m_w = 0.0f;
+        }
+
+        u32x4 v[W][VPT];
+        float wt[W];
+        // The row address is computed whether or not the slot is valid (an
+        // empty resource never dereferences it): a select between it and a
+        // constant would be turned into a branch, and branches between the
+        // slots would let the compiler sink each slot's FMAs past the loads
+        // that follow them.
+        const uint64_t rows = reinterpret_cast<uintptr_t>(a.rows);
+        auto issue = [&](int s) {
+            const int b = s % W;
+            const float w = lane_value(m_w, s);
+            bool ok;
+            int64_t off;   // elements
+            if constexpr (kIdx) {
+                const int32_t i = lane_value(m_idx, s);
+                ok = i >= 0 && (int64_t)i < a.num_rows;
+                off = (int64_t)i * a.row_stride;
+            } else {
+                ok = KC > 0 || s < top_k;
+                off = (tk + s) * (int64_t)a.hidden;
+            }
+            wt[b] = ok ? w : 0.0f;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<void *>(rows + 2 * (uint64_t)off), 0, ok ? nv * 16 : 0,
+                kRawBufferWord3);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)   // vectors past the row read as zeros
+                v[b][i] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + i * team) * 16, 0,
+                                                                MF_ROW_LOAD_POLICY);
+        };
+#pragma unroll
+        for (int s = 0; s < W; ++s)
+            issue(s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kSlotsMax; ++s) {
+            const int b = s % W;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[i][e] = __builtin_fmaf(wt[b], elem(v[b][i], e), acc[i][e]);
+                // An empty statement that reads and writes the sums keeps this
+                // slot's FMAs here: otherwise instruction selection may place
+                // every slot's FMAs after the last barrier, with all 32 slots'
+                // rows held in registers.
+                asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]),
+                             "+v"(acc[i][3]), "+v"(acc[i][4]), "+v"(acc[i][5]),
+                             "+v"(acc[i][6]), "+v"(acc[i][7]));
+            }
+            if (s + W < kSlotsMax)
+                issue(s + W);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // Batches of KB slots (one batch when every slot fits): uniform
+        // per-slot data first (scalar loads, one wait), then every valid
+        // slot's row vectors, then the FMAs in ascending slot order.  The
+        // batches are unrolled up to the slots the kernel serves, with a
+        // uniform exit past a run-time top-k.
+#pragma unroll
+        for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
+            if (KC < 0 && k0 >= top_k)
+                break;
+            int64_t row_off[KB];   // elements
+            bool ok[KB];
+            float w[KB];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                // Slots past a run-time top-k re-read the token's last slot
+                // (always in bounds) and are masked: the metadata loads stay
+                // unconditional, so they issue together behind one wait.
+                const int k = k0 + b;
+                const bool live = KC > 0 || k < top_k;
+                const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
+                if constexpr (kIdx) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                    const int32_t i = a.idx[tk + kk];
+                    ok[b] = live && i >= 0 && (int64_t)i < a.num_rows;
+                    row_off[b] = (int64_t)i * a.row_stride;
+                } else if constexpr (L == Layout::kTokenMajor) {
+                    w[b] = load_weight<W_BF16>(a.weights, tk + kk);
+                    ok[b] = live;
+                    row_off[b] = (tk + kk) * (int64_t)a.hidden;
+                } else {   // kDirect
+                    w[b] = 1.0f;
+                    ok[b] = live;
+                    row_off[b] = t * a.row_stride;
+                }
+            }
+            u32x4 v[KB][VPT];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (ok[b]) {
+                    const u32x4 *r = reinterpret_cast<const u32x4 *>(a.rows + row_off[b]);
+#pragma unroll
+                    for (int i = 0; i < VPT; ++i) {
+                        const int j = lane + i * team;
+                        if (EXACT || j < nv)
+                            v[b][i] = load_row_vec(r + j);
+                        else
+                            v[b][i] = (u32x4){0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (ok[b]) {
+#pragma unroll
+                    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[i][e] = __builtin_fmaf(w[b], elem(v[b][i], e), acc[i][e]);
+                }
+            }
+            // Every gather of this batch has been consumed.  Saying so keeps
+            // the compiler, which cannot pair each conditional load with its
+            // conditional use, from waiting before each gather of the next
+            // batch.
+            if constexpr (kSlotsMax > KB)
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+    }
+
+    finish_token<EPI, VPT, EXACT>(acc, gv, rv, a, t, lane, team, nv);
 }
 
 // ------------------------------------------------------------ dispatch ---

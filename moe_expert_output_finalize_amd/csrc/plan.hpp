@@ -29,17 +29,12 @@
 #ifndef MF_INDEX_MAP_VPT1_MAX_HIDDEN
 #define MF_INDEX_MAP_VPT1_MAX_HIDDEN 4096
 #endif
-// Where a token has more slots than fit in flight at once, index-map slots
-// stream through a rolling window of this many slots (by vectors per thread:
-// one, two), and token-major slots arrive in batches (a token's rows are one
-// contiguous block, fetched fastest in bursts: a rolling window measured 4 %
-// slower at top-k 16 and hidden 2048, and no faster at any other shape).
-#ifndef MF_ROLL_INDEX_MAP
-#define MF_ROLL_INDEX_MAP 1
-#endif
-#ifndef MF_ROLL_TOKEN_MAJOR
-#define MF_ROLL_TOKEN_MAJOR 0
-#endif
+// Slots an index-map workgroup keeps in flight, by vectors per thread (one,
+// two): a token with more slots streams them through a rolling window of
+// this many.  Token-major tokens with more slots than fit arrive in batches
+// instead: a token's rows are one contiguous block, fetched fastest in
+// bursts (a rolling window measured 4 % slower at top-k 16 and hidden 2048,
+// and no faster at any other shape).
 #ifndef MF_ROLL_WINDOW_VPT1
 #define MF_ROLL_WINDOW_VPT1 16
 #endif
@@ -90,28 +85,28 @@ constexpr int kc_for_topk(int top_k)
          : top_k <= 12 ? -12 : top_k <= 16 ? -16 : top_k <= 24 ? -24 : -32;
 }
 
-constexpr bool streams(bool index_map) { return index_map ? MF_ROLL_INDEX_MAP : MF_ROLL_TOKEN_MAJOR; }
-
-// Whether a token's slots stream through a rolling window instead of
-// arriving in one batch or in several: more slots than fit in flight, on a
-// layout that streams.
-constexpr bool rolling(bool index_map, int kc, int vpt)
+// The index-map window for `vpt` vectors per thread.
+constexpr int window(int vpt)
 {
-    return streams(index_map) && (kc < 0 ? -kc : kc) * vpt > max_vecs(index_map, vpt);
+    return vpt == 1 ? MF_ROLL_WINDOW_VPT1 : vpt == 2 ? MF_ROLL_WINDOW_VPT2 : MF_MAX_VECS_INDEX_MAP / vpt;
 }
 
-// Slots whose rows one workgroup has in flight at once: all -KC (or KC) when
-// they fit in max_vecs, else the rolling window, else batches of max_vecs /
-// VPT slots.
+// Whether a token's slots stream through a rolling window (index map, more
+// slots than the window) instead of arriving in one batch or several.
+constexpr bool rolling(bool index_map, int kc, int vpt)
+{
+    return index_map && (kc < 0 ? -kc : kc) > window(vpt);
+}
+
+// Slots whose rows one workgroup has in flight at once: all of a token's
+// when they fit (the window on the index map, max_vecs on token-major
+// rows), else the window, else batches of max_vecs / VPT slots.
 constexpr int slots_in_flight(bool index_map, int kc, int vpt)
 {
     const int want = kc < 0 ? -kc : kc;
-    if (want * vpt <= max_vecs(index_map, vpt))
-        return want;
-    if (rolling(index_map, kc, vpt))
-        return vpt == 1 ? MF_ROLL_WINDOW_VPT1 : vpt == 2 ? MF_ROLL_WINDOW_VPT2
-                                                          : max_vecs(index_map, vpt) / vpt;
-    return max_vecs(index_map, vpt) / vpt;
+    if (index_map)
+        return want <= window(vpt) ? want : window(vpt);
+    return want * vpt <= max_vecs(false, vpt) ? want : max_vecs(false, vpt) / vpt;
 }
 
 constexpr int max_team(int vpt) { return vpt == 1 ? 1024 : vpt == 2 ? 512 : 256; }
