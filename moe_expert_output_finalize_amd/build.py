@@ -50,15 +50,42 @@ def source_files(root: str = ROOT) -> list[str]:
     return files
 
 
+def code_text(text: str) -> str:
+    """C/C++ source with its comments removed and blank lines dropped, so that
+    an edit to a comment does not change what the digest says was built.
+    String and character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    lines = [line.rstrip() for line in "".join(out).splitlines()]
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest(root: str = ROOT, defines: list[str] | None = None) -> str:
-    """SHA-256 over the names and contents of the library's sources, the
-    compiler flags and any extra definitions."""
+    """SHA-256 over the names and code (comments removed) of the library's
+    sources, the compiler flags and any extra definitions."""
     h = hashlib.sha256()
     h.update(" ".join(HIPCC_FLAGS + sorted(defines or [])).encode())
     for path in source_files(root):
         h.update(os.path.relpath(path, root).encode() + b"\0")
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode() + b"\0")
     return h.hexdigest()
 
 

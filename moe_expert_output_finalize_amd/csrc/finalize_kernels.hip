@@ -16,11 +16,16 @@
 //  - one workgroup per token; hidden/8 threads-or-fewer each own VPT 16-byte
 //    column vectors of the token (vector j = lane + i * blockDim), so every
 //    wave reads 1 KiB contiguous runs of each gathered row;
-//  - the token's indices and weights are uniform, so they live in SGPRs and
-//    validity is a scalar branch: invalid slots issue no memory traffic;
-//  - up to 16 row vectors per thread are in flight before the first FMA:
-//    all of a token's rows at top-k 8, and at top-k 16 with one vector per
-//    thread (index map up to hidden 4096); larger top-k in batches;
+//  - the token's indices and weights are uniform, so they live in SGPRs (or
+//    in VGPR lanes read back per slot) and validity is a scalar decision:
+//    invalid slots issue no memory traffic;
+//  - up to 16 row vectors per thread are in flight: all of a token's rows
+//    when they fit (top-k 8 everywhere, top-k 16 at one vector per thread);
+//    otherwise index-map slots stream through a rolling window (the rows of
+//    slot s + W are issued once slot s is reduced) and token-major slots,
+//    one contiguous block per token, arrive in batches;
+//  - a call whose grid would exceed 2^31 work-items runs as several
+//    launches, each finalizing the tokens from its token_base on;
 //  - the FP32 sum, the sum of squares and the normalised values stay in
 //    VGPRs; the cross-lane sum uses DPP row operations, the cross-wave sum
 //    one LDS exchange and barrier;

@@ -38,15 +38,26 @@ def test_current_library_is_accepted(tmp_path):
 def test_edited_source_is_refused(tmp_path, rel):
     lib = copy_tree(str(tmp_path))
     with open(os.path.join(str(tmp_path), rel), "a") as f:
-        f.write("\n// edited after the build\n")
+        f.write("\nstatic const int mf_edited_after_the_build = 1;\n")
     with pytest.raises(ImportError, match="other sources"):
         mf.check_built(lib)
+
+
+def test_comment_edit_is_accepted(tmp_path):
+    """The digest covers code, not comments: an edited comment leaves the
+    built library (and the measurements taken on it) current."""
+    lib = copy_tree(str(tmp_path))
+    path = os.path.join(str(tmp_path), "moe_expert_output_finalize_amd", "csrc",
+                        "finalize_kernels.hip")
+    with open(path, "a") as f:
+        f.write("\n// a comment added after the build\n/* and a block comment */\n")
+    mf.check_built(lib)
 
 
 def test_import_of_a_stale_tree_raises(tmp_path):
     lib = copy_tree(str(tmp_path))
     with open(os.path.join(os.path.dirname(lib), "csrc", "capi.cpp"), "a") as f:
-        f.write("\n")
+        f.write("\nstatic const int mf_edited_after_the_build = 1;\n")
     r = import_from(str(tmp_path))
     assert r.returncode != 0 and "ImportError" in r.stderr and "other sources" in r.stderr
 
