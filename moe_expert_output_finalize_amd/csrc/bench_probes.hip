@@ -240,7 +240,8 @@ __attribute__((visibility("default"))) int mf_probe_mixed(const void *in, void *
     }
 }
 
-// tokens workgroups of `threads` threads; mode 0 reads tokens x ratio rows
+// tokens workgroups of `threads` threads (at most 2^31 work-items in all,
+// the finalize launcher's limit per launch); mode 0 reads tokens x ratio rows
 // of `in`, 1 writes tokens x ratio rows of `out`, 2 reads tokens x ratio rows
 // and writes tokens rows.  A row is threads x 16 bytes; the output stays
 // below 4 GiB.  lds_bytes of dynamic LDS per workgroup (0: none).
@@ -249,7 +250,7 @@ __attribute__((visibility("default"))) int mf_probe_rows(int mode, int ratio, in
                                                           int64_t tokens, int threads,
                                                           int64_t lds_bytes, void *stream)
 {
-    if (tokens <= 0 || tokens > INT32_MAX || threads < 64 || threads > 1024 ||
+    if (tokens <= 0 || tokens * threads > (int64_t(1) << 31) || threads < 64 || threads > 1024 ||
         threads % 64 != 0 || lds_bytes < 0 || lds_bytes > 160 * 1024 || mode < 0 || mode > 2)
         return (int)hipErrorInvalidValue;
     if ((mode != 1 && !in) || (mode != 0 && !out) || (mode == 0 && !flag))
