@@ -578,35 +578,48 @@ finalize_kernel(const FinalizeArgs a)
 
 // ------------------------------------------------------------ dispatch ---
 
-// Dynamic LDS that caps the resident workgroups per CU (plan.hpp), from the
-// device's LDS limits, queried once per device; concurrent first calls
-// store the same values.
-size_t residency_lds_bytes(int hidden, int slots)
+// The current device's LDS per CU and per workgroup and its CU count,
+// queried once per device (concurrent first calls store the same values);
+// all zero if a query fails, and then no residency cap applies.
+struct DeviceLimits {
+    int lds_per_cu, lds_per_block, cus;
+};
+
+DeviceLimits device_limits()
 {
-    static std::atomic<int> lds_per_cu[64], lds_per_block[64];
+    static std::atomic<int> cached[64][3];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 0;
-    int cu = lds_per_cu[dev].load(std::memory_order_relaxed);
-    int blk = lds_per_block[dev].load(std::memory_order_relaxed);
-    if (cu <= 0 || blk <= 0) {
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-                hipSuccess ||
-            hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-                hipSuccess || cu <= 0 || blk <= 0)
-            return 0;
-        lds_per_cu[dev].store(cu, std::memory_order_relaxed);
-        lds_per_block[dev].store(blk, std::memory_order_relaxed);
-    }
-    return (size_t)residency_lds(hidden, slots, cu, blk, kStaticLds);
+        return DeviceLimits{};
+    DeviceLimits d{cached[dev][0].load(std::memory_order_relaxed),
+                   cached[dev][1].load(std::memory_order_relaxed),
+                   cached[dev][2].load(std::memory_order_relaxed)};
+    if (d.lds_per_cu > 0 && d.lds_per_block > 0 && d.cus > 0)
+        return d;
+    if (hipDeviceGetAttribute(&d.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess ||
+        hipDeviceGetAttribute(&d.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        d.lds_per_cu <= 0 || d.lds_per_block <= 0 || d.cus <= 0)
+        return DeviceLimits{};
+    cached[dev][0].store(d.lds_per_cu, std::memory_order_relaxed);
+    cached[dev][1].store(d.lds_per_block, std::memory_order_relaxed);
+    cached[dev][2].store(d.cus, std::memory_order_relaxed);
+    return d;
 }
 
 // Launch the kernel of plan p over all tokens, at most p.max_tokens per
-// launch (each launch starts at its token_base).
+// launch (each launch starts at its token_base), with the dynamic LDS that
+// sets the workgroups resident per CU (plan.hpp).
 template <Layout L, bool W_BF16, Epilogue EPI, int KC>
 hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s)
 {
-    const size_t lds = residency_lds_bytes(a.hidden, p.slots);
+    const DeviceLimits d = device_limits();
+    const int64_t blocks =
+        residency_blocks(L == Layout::kIndexMap, a.hidden, p.slots, a.num_tokens, d.cus);
+    const size_t lds =
+        (size_t)residency_lds(blocks, d.lds_per_cu, d.lds_per_block, kStaticLds);
     FinalizeArgs c = a;
     for (int64_t t0 = 0; t0 < a.num_tokens; t0 += p.max_tokens) {
         c.token_base = t0;

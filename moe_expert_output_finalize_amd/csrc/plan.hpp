@@ -45,6 +45,11 @@
 #define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
                                   // loads in flight total about this much per CU
 #endif
+// An index-map call whose tokens fit on the device at up to this many
+// workgroups per CU runs them all in one round instead (0: off).
+#ifndef MF_ONE_ROUND_MAX_BLOCKS
+#define MF_ONE_ROUND_MAX_BLOCKS 8
+#endif
 
 namespace mf {
 
@@ -197,21 +202,42 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
     return p;
 }
 
-// Dynamic LDS to reserve per workgroup so that a CU holds
-// ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup) workgroups,
-// clamped to 2..16, given the device's LDS per CU and per workgroup and the
-// kernel's own static LDS.  Beyond that, extra concurrent gathers do not
-// raise bandwidth; they stretch every token's lifetime and with it the tail
-// of the launch (measured: 2-5 % faster on every large workload than
-// residency limited by registers).  0 when no cap applies.
-constexpr int64_t residency_lds(int hidden, int slots, int64_t lds_per_cu,
-                                int64_t lds_per_block, int64_t static_lds)
+// Workgroups a CU should hold, 0 for no cap.  Normally
+// ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup), clamped to
+// 2..16: beyond that, extra concurrent gathers do not raise bandwidth; they
+// stretch every token's lifetime and with it the tail of the launch
+// (measured: 2-5 % faster on every large workload than residency limited by
+// registers).  But an index-map call with more tokens than that holds on
+// the device's `cus` CUs, yet no more than MF_ONE_ROUND_MAX_BLOCKS per CU,
+// gets ceil(tokens / cus): all of its tokens start at once, with no second
+// round whose last workgroups run on a nearly idle device (registers may
+// still hold fewer; measured 1-4 % faster at hidden 4096 / top-k 8 and 3-10 %
+// at hidden 2048 / top-k 16 for 585-2048 tokens; token-major rows gained
+// nothing consistent).
+constexpr int64_t residency_blocks(bool index_map, int hidden, int slots, int64_t tokens,
+                                   int cus)
 {
-    if (MF_INFLIGHT_KB_PER_CU <= 0 || lds_per_cu <= 0 || lds_per_block <= 0)
+    if (MF_INFLIGHT_KB_PER_CU <= 0 || hidden <= 0 || slots <= 0)
         return 0;
     const int64_t per_block = 2LL * hidden * slots;   // row bytes in flight
     const int64_t want = ((int64_t)MF_INFLIGHT_KB_PER_CU * 1024 + per_block - 1) / per_block;
     const int64_t blocks = want < 2 ? 2 : want > 16 ? 16 : want;
+    if (index_map && cus > 0 && tokens > blocks * cus) {
+        const int64_t need = (tokens + cus - 1) / cus;
+        if (need <= MF_ONE_ROUND_MAX_BLOCKS)
+            return need;
+    }
+    return blocks;
+}
+
+// Dynamic LDS to reserve per workgroup so that a CU holds `blocks`
+// workgroups (residency_blocks), given the device's LDS per CU and per
+// workgroup and the kernel's own static LDS.  0 when no cap applies.
+constexpr int64_t residency_lds(int64_t blocks, int64_t lds_per_cu, int64_t lds_per_block,
+                                int64_t static_lds)
+{
+    if (blocks <= 0 || lds_per_cu <= 0 || lds_per_block <= 0)
+        return 0;
     // Leave 1 KiB of the CU's share unclaimed, and never ask for more than a
     // workgroup may hold besides the kernel's own LDS.
     int64_t lds = lds_per_cu / blocks - 1024;

@@ -27,6 +27,7 @@ struct Record {
     int kc, vpt, team;
     int64_t launches;    // kernel launches the last call was split into
     int64_t max_tokens;  // tokens per launch at most
+    int64_t blocks;      // workgroups per CU the launcher reserves LDS for, 256 CUs
     int violations;      // contract violations seen since the last reset
     int fail_next;       // error code the next call returns (0: none)
 };
@@ -81,6 +82,7 @@ int launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, void *st
     r.vpt = p.vpt;
     r.team = p.team;
     r.max_tokens = p.max_tokens;
+    r.blocks = residency_blocks(idx_map, a.hidden, p.slots, a.num_tokens, 256);
     r.launches = 0;
     int64_t covered = 0;
     for (int64_t t0 = 0; t0 < a.num_tokens; t0 += p.max_tokens) {
@@ -110,13 +112,14 @@ void mf_test_reset(void) { memset(&g_rec, 0, sizeof g_rec); }
 // Make the next launch fail with `code` (non-zero).
 void mf_test_fail_next_launch(int code) { g_rec.fail_next = code; }
 
-// The record, as 12 int64 values: calls, layout, epilogue, num_tokens, hidden,
-// top_k, kc, vpt, team, launches, max_tokens, violations.
+// The record, as 13 int64 values: calls, layout, epilogue, num_tokens, hidden,
+// top_k, kc, vpt, team, launches, max_tokens, blocks, violations.
 void mf_test_record(int64_t *out)
 {
     const Record &r = g_rec;
-    const int64_t v[12] = {r.calls, r.layout, r.epi, r.num_tokens, r.hidden, r.top_k,
-                           r.kc,    r.vpt,    r.team, r.launches, r.max_tokens, r.violations};
+    const int64_t v[13] = {r.calls,    r.layout, r.epi,      r.num_tokens, r.hidden,
+                           r.top_k,    r.kc,     r.vpt,      r.team,       r.launches,
+                           r.max_tokens, r.blocks, r.violations};
     memcpy(out, v, sizeof v);
 }
 

@@ -97,10 +97,10 @@ def host():
 
 
 def record(lib) -> dict:
-    buf = (ctypes.c_int64 * 12)()
+    buf = (ctypes.c_int64 * 13)()
     lib.mf_test_record(buf)
     keys = ("calls", "layout", "epi", "num_tokens", "hidden", "top_k", "kc", "vpt", "team",
-            "launches", "max_tokens", "violations")
+            "launches", "max_tokens", "blocks", "violations")
     return dict(zip(keys, list(buf)))
 
 
@@ -165,6 +165,29 @@ def test_launch_plan(host, fn, over, kc, vpt, team):
     assert cc.ctypes_call(host, fn, over) == cc.OK
     rec = record(host)
     assert (rec["kc"], rec["vpt"], rec["team"]) == (kc, vpt, team), rec
+
+
+# Workgroups per CU the launcher reserves LDS for on a 256-CU device: about
+# 128 KiB of rows in flight per CU (2..16 workgroups), or, for an index-map
+# call whose tokens all fit at up to 8 per CU, ceil(tokens / 256).
+@pytest.mark.parametrize("fn,over,blocks", [
+    ("moe_finalize_rmsnorm", dict(T=8192), 2),                      # 8 x 8 KiB rows: cap 2
+    ("moe_finalize_rmsnorm", dict(T=512), 2),                       # one round already
+    ("moe_finalize_rmsnorm", dict(T=513), 3),
+    ("moe_finalize_rmsnorm", dict(T=585), 3),
+    ("moe_finalize_rmsnorm", dict(T=2048), 8),
+    ("moe_finalize_rmsnorm", dict(T=2049), 2),                      # would need 9 per CU
+    ("moe_finalize", dict(H=2048, stride=2048, K=16, T=1170), 5),   # 16 x 4 KiB: cap 2
+    ("moe_finalize", dict(H=4096, K=2, T=4096), 8),                 # 2 x 8 KiB: cap 8
+    ("moe_finalize", dict(H=256, stride=256, K=1, T=8192), 16),     # tiny rows: cap 16
+    ("beam_moe_finalize", dict(cap=1024, wrows=1024, live=585), 2), # token major: cap only
+    ("mf_rmsnorm", dict(T=585), 16),                                # one 8 KiB row: cap 16
+])
+def test_residency(host, fn, over, blocks):
+    host.mf_test_reset()
+    assert cc.ctypes_call(host, fn, over) == cc.OK
+    rec = record(host)
+    assert rec["violations"] == 0 and rec["blocks"] == blocks, rec
 
 
 def test_failed_launch_is_reported(host):

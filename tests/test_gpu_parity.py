@@ -254,7 +254,9 @@ def test_consumer_alone_matches_oracle():
 
 # ------------------------------------------------------------ edge cases ----
 
-@pytest.mark.parametrize("T", [1, 7, 8, 9, 13, 257])
+# 585 and 2048 tokens run in one round at 3 and 8 workgroups per CU (a
+# 256-CU device), 2049 at the usual residency.
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 13, 257, 585, 2048, 2049])
 def test_ragged_token_counts(T):
     c = wl.tiny(num_tokens=T, num_rows=8 * T + 3, invalid_frac=0.05, poison=True,
                 nan_rows_beyond=2)
