@@ -210,10 +210,15 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
 // registers).  But an index-map call with more tokens than that holds on
 // the device's `cus` CUs, yet no more than MF_ONE_ROUND_MAX_BLOCKS per CU,
 // gets ceil(tokens / cus): all of its tokens start at once, with no second
-// round whose last workgroups run on a nearly idle device (registers may
-// still hold fewer; measured 1-4 % faster at hidden 4096 / top-k 8 and 3-10 %
-// at hidden 2048 / top-k 16 for 585-2048 tokens; token-major rows gained
-// nothing consistent).
+// round whose last workgroups run on a nearly idle device.  Registers may
+// still hold fewer, and the raised cap then still shortens the rounds.
+// Measured for 585-2048 tokens: 1-3 % faster at hidden 4096 / top-k 8, 4-10 %
+// at hidden 2048 / top-k 16, up to 7 % at hidden 2048 / top-k 32 (768
+// tokens); within 1.4 % either way at hidden 4096 / top-k 16, whose cap
+// already holds more than the target in flight; at hidden 4096 / top-k 4,
+// 5 % faster at 1170 tokens and 2 % slower at 1560.  Raising it only where
+// the kernel's occupancy confirms a single round gave up most of the gains;
+// token-major rows gained nothing consistent.
 constexpr int64_t residency_blocks(bool index_map, int hidden, int slots, int64_t tokens,
                                    int cus)
 {
