@@ -3,14 +3,14 @@
 // Plain C++ with no HIP types: every check runs on the host before any HIP
 // call, so a rejected call has no side effect, and the tests can build this
 // file with an ordinary host compiler under AddressSanitizer and
-// UndefinedBehaviorSanitizer against a recording stand-in for the launcher.  The checks are the C form of the parameter contracts on
-// the FlashInfer page "flashinfer.comm.tp_moe_finalize_rmsnorm" (Parameters:
-// shapes, dtypes, unit-stride rows with a row stride that is a multiple of 8
-// elements, 16-byte alignment) and of the argument
-// checks in beam_moe_finalize on the vLLM page
-// "vllm.models.beam.nvidia.moe_finalize" (1 <= top_k <= 32, hidden a
-// multiple of 256 in [256, 8192], live rows <= capacity, weight rows >= live
-// rows, post_weight only with a norm, nothing to do for zero live rows).
+// UndefinedBehaviorSanitizer against a recording stand-in for the launcher.
+// The checks are the C form of the parameter contracts on the FlashInfer
+// page "flashinfer.comm.tp_moe_finalize_rmsnorm" (Parameters: shapes, dtypes,
+// unit-stride rows with a row stride that is a multiple of 8 elements,
+// 16-byte alignment) and of the argument checks in beam_moe_finalize on the
+// vLLM page "vllm.models.beam.nvidia.moe_finalize" (1 <= top_k <= 32, hidden
+// a multiple of 256 in [256, 8192], live rows <= capacity, weight rows >=
+// live rows, post_weight only with a norm, nothing to do for zero live rows).
 // The FlashInfer page specialises its finalize+RMSNorm to hidden 4096 and
 // top-k 8; here every entry point accepts the wider envelope of the vLLM
 // checks, 4096 / 8 included.
