@@ -265,6 +265,23 @@ def test_ragged_token_counts(T):
     assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"T={T}")
 
 
+# Index-map calls of a few hundred to two thousand tokens take the one-round
+# residency (all tokens resident at once, up to 8 workgroups per CU on a
+# 256-CU device) in every kernel kind: compile-time top-k 16 (5 per CU),
+# run-time top-k sized for 12 slots (4 per CU), for 8 slots at two vectors
+# per thread (6 per CU), the rolling window at hidden 7168 (3 per CU asked,
+# registers hold 2), and tiny rows whose cap already holds them (16 per CU).
+@pytest.mark.parametrize("H,K,T", [(2048, 16, 1170), (2048, 12, 1000), (4096, 5, 1300),
+                                   (7168, 32, 585), (256, 1, 4000)])
+def test_one_round_residency_shapes(H, K, T):
+    c = wl.make_index_map_case(7000 + H + K, num_tokens=T, hidden=H, top_k=K,
+                               num_rows=T * K + 7, row_stride=H + 8, weights_dtype="fp32",
+                               invalid_frac=0.05, poison=True, nan_rows_beyond=2)
+    d = IndexMapOnDevice(c)
+    assert_within_ulp(gpu_rmsnorm(d), oracle_rmsnorm(c), 1, NORM_MIN_EXACT, f"H={H} K={K} T={T}")
+    assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"H={H} K={K} T={T}")
+
+
 def test_all_invalid_tokens_and_empty_row_matrix():
     c = wl.tiny(num_tokens=12, num_rows=96)
     c.idx[3, :] = -1
