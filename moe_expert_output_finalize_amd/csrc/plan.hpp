@@ -204,10 +204,13 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
 
 // Workgroups a CU should hold, 0 for no cap.  Normally
 // ceil(MF_INFLIGHT_KB_PER_CU / in-flight bytes per workgroup), clamped to
-// 2..16: beyond that, extra concurrent gathers do not raise bandwidth; they
+// 2..32: beyond that, extra concurrent gathers do not raise bandwidth; they
 // stretch every token's lifetime and with it the tail of the launch
 // (measured: 2-5 % faster on every large workload than residency limited by
-// registers).  But an index-map call with more tokens than that holds on
+// registers).  The upper end is the 32 waves a CU holds: small rows run one-
+// wave workgroups, and a clamp at 16 left them half the bytes in flight
+// (hidden 256: 13-27 % slower, hidden 512 / top-k 2: 13 %).  But an
+// index-map call with more tokens than that holds on
 // the device's `cus` CUs, yet no more than MF_ONE_ROUND_MAX_BLOCKS per CU,
 // gets ceil(tokens / cus): all of its tokens start at once, with no second
 // round whose last workgroups run on a nearly idle device.  Registers may
@@ -226,7 +229,7 @@ constexpr int64_t residency_blocks(bool index_map, int hidden, int slots, int64_
         return 0;
     const int64_t per_block = 2LL * hidden * slots;   // row bytes in flight
     const int64_t want = ((int64_t)MF_INFLIGHT_KB_PER_CU * 1024 + per_block - 1) / per_block;
-    const int64_t blocks = want < 2 ? 2 : want > 16 ? 16 : want;
+    const int64_t blocks = want < 2 ? 2 : want > 32 ? 32 : want;
     if (index_map && cus > 0 && tokens > blocks * cus) {
         const int64_t need = (tokens + cus - 1) / cus;
         if (need <= MF_ONE_ROUND_MAX_BLOCKS)
