@@ -598,9 +598,10 @@ def dispatch_stats(torch, step, first: int, steps: int) -> dict:
             "mean_us": sum(us) / len(us), "dispatches": len(us)}
 
 
-ENVELOPE_HIDDEN = (2048, 4096, 7168)
+ENVELOPE_HIDDEN = (256, 512, 1024, 2048, 4096, 7168, 8192)
 ENVELOPE_TOPK = (1, 2, 4, 6, 8, 12, 16, 32)
 ENVELOPE_ROW_BYTES = 256 << 20      # gathered row bytes per launch (before rotation)
+ENVELOPE_MAX_TOKENS = 1 << 17       # hidden 256 at top-k 1-2, 512 at 1: 64-128 MiB of rows
 ENVELOPE_SPANS = 5
 
 
@@ -609,7 +610,9 @@ def envelope(torch, mf, wl, steps: int, warmup: int, shapes: str = "",
     """Fused kernel time over hidden x top-k on both layouts: index map
     (expert-grouped Zipf 1.1 map, FP32 weights, RMSNorm) and token major
     (post-norm).  Inputs are seeded N(0,1) rows made on the device; the
-    token count gives about 256 MiB of gathered rows per launch, and steps
+    token count gives about 256 MiB of gathered rows per launch (at most
+    ENVELOPE_MAX_TOKENS tokens, so hidden 256 at top-k 1 and 2 and hidden
+    512 at top-k 1 carry 64-128 MiB), and steps
     rotate over copies totalling at least 1.5 GiB, as in the main bench.  A
     cell's time is the median of ENVELOPE_SPANS spans of steps / ENVELOPE_SPANS
     back-to-back launches.  The rows are drawn in BF16 in place and every
@@ -629,7 +632,7 @@ def envelope(torch, mf, wl, steps: int, warmup: int, shapes: str = "",
             cells.append((layout, int(H), int(K)))
     for layout, H, K in cells:
         counts = ([int(t) for t in tokens.split(",")] if tokens else
-                  [max(256, min(32768, ENVELOPE_ROW_BYTES // (K * H * 2)))])
+                  [max(256, min(ENVELOPE_MAX_TOKENS, ENVELOPE_ROW_BYTES // (K * H * 2)))])
         for T in counts:
             gen.manual_seed(1000 * H + K)
             rng = np.random.Generator(np.random.PCG64(1000 * H + K))
