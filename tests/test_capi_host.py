@@ -169,8 +169,9 @@ def test_launch_plan(host, fn, over, kc, vpt, team):
 
 # Workgroups per CU the launcher reserves LDS for on a 256-CU device: about
 # 128 KiB of rows in flight per CU (2..32 workgroups, 32 being the waves a
-# CU holds), or, for an index-map call that fits at up to 8 per CU, all of
-# its tokens at once: ceil(tokens / 256).
+# CU holds; 32 outright for workgroups with at most 8 KiB of rows in
+# flight), or, for an index-map call that fits at up to 8 per CU, all of its
+# tokens at once: ceil(tokens / 256).
 @pytest.mark.parametrize("fn,over,blocks", [
     ("moe_finalize_rmsnorm", dict(T=8192), 2),                      # 8 x 8 KiB rows: cap 2
     ("moe_finalize_rmsnorm", dict(T=512), 2),                       # one round already
@@ -182,7 +183,9 @@ def test_launch_plan(host, fn, over, kc, vpt, team):
     ("moe_finalize", dict(H=4096, K=2, T=4096), 8),                 # 2 x 8 KiB: cap 8
     ("moe_finalize", dict(H=256, stride=256, K=1, T=8192), 32),     # tiny rows: cap 32
     ("beam_moe_finalize", dict(cap=1024, wrows=1024, live=585), 2), # token major: cap only
-    ("mf_rmsnorm", dict(T=585), 16),                                # one 8 KiB row: 16
+    ("mf_rmsnorm", dict(T=585), 32),                                # one 8 KiB row: 32
+    ("moe_finalize", dict(H=256, stride=256, K=12, T=4096), 32),    # 12 x 512 B rows
+    ("moe_finalize", dict(H=512, stride=512, K=10, T=4096), 13),    # 10 x 1 KiB rows
     ("mf_rmsnorm", dict(H=2048, stride=2048, T=585), 32),           # one 4 KiB row: 32
     ("moe_finalize", dict(H=512, stride=512, K=2, T=4096), 32),     # 2 x 1 KiB rows
 ])
