@@ -119,6 +119,19 @@ __device__ __forceinline__ void store_out_vec(__amdgpu_buffer_rsrc_t row, uint32
     __builtin_amdgcn_raw_buffer_store_b128(v, row, byte_off, 0, MF_STORE_POLICY);
 }
 
+// Vector j of a row of nv 16-byte vectors at p, or zeros for j >= nv: a
+// buffer load bounded at the row's end, for teams with more threads than
+// vectors.  A per-lane branch instead (load, else zero the registers) makes
+// the compiler drain every load in flight before the zeroing, which
+// serialised a token's gathers.
+template <int POL>
+__device__ __forceinline__ u32x4 load_vec_bounded(const void *p, int nv, int j)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, nv * 16, kRawBufferWord3);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, j * 16, 0, POL);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load_weight(const void *w, int64_t i)
 {
@@ -190,10 +203,10 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                                    EPI == Epilogue::kResidualNorm;
     const __amdgpu_buffer_rsrc_t out_row =
         row_resource(a.out + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
+    // Lanes past the row (teams with more threads than vectors) store
+    // outside the resource, which drops them.
     auto store = [&](int i, const u32x4 &o) {
-        const int j = lane + i * team;
-        if (EXACT || j < nv)
-            store_out_vec(out_row, (uint32_t)j * 16u, o);
+        store_out_vec(out_row, (uint32_t)(lane + i * team) * 16u, o);
     };
 
     if constexpr (EPI == Epilogue::kRound) {
@@ -279,8 +292,9 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
         for (int i = 0; i < VPT; ++i) {
             const int j = lane + i * team;
             nv2[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (a.gain2 && (EXACT || j < nv))
-                nv2[i] = reinterpret_cast<const u32x4 *>(a.gain2)[j];
+            if (a.gain2)
+                nv2[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain2)[j]
+                               : load_vec_bounded<0>(a.gain2, nv, j);
         }
         float ss = 0.0f;
 #pragma unroll
@@ -304,9 +318,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                 }
                 o[q] = pack_bf16x2(y0, y1);
             }
-            const int j = lane + i * team;
-            if (EXACT || j < nv)
-                store_out_vec(out2_row, (uint32_t)j * 16u, o);
+            store_out_vec(out2_row, (uint32_t)(lane + i * team) * 16u, o);
         }
         return;
     }
@@ -404,8 +416,9 @@ finalize_kernel(const FinalizeArgs a)
         for (int i = 0; i < VPT; ++i) {
             const int j = lane + i * team;
             gv[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (have && (EXACT || j < nv))
-                gv[i] = reinterpret_cast<const u32x4 *>(a.gain)[j];
+            if (have)
+                gv[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain)[j]
+                              : load_vec_bounded<0>(a.gain, nv, j);
         }
     }
 
@@ -416,9 +429,7 @@ finalize_kernel(const FinalizeArgs a)
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int j = lane + i * team;
-            rv[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (EXACT || j < nv)
-                rv[i] = load_row_vec(rr + j);
+            rv[i] = EXACT ? load_row_vec(rr + j) : load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, nv, j);
         }
     }
 
@@ -547,10 +558,8 @@ finalize_kernel(const FinalizeArgs a)
 #pragma unroll
                     for (int i = 0; i < VPT; ++i) {
                         const int j = lane + i * team;
-                        if (EXACT || j < nv)
-                            v[b][i] = load_row_vec(r + j);
-                        else
-                            v[b][i] = (u32x4){0u, 0u, 0u, 0u};
+                        v[b][i] = EXACT ? load_row_vec(r + j)
+                                        : load_vec_bounded<MF_ROW_LOAD_POLICY>(r, nv, j);
                     }
                 }
             }

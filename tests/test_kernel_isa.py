@@ -18,7 +18,10 @@ instruction:
   vector, and the wait before each slot's FMAs leaves the rest of the window
   in flight;
 - a token-major token with more slots than fit arrives in batches: the
-  second batch's loads follow a full drain of the first's.
+  second batch's loads follow a full drain of the first's;
+- a team with more threads than vectors (hidden / 256 odd: the last half
+  wave idle) reads its rows through buffer loads bounded at the row's end,
+  and issues every gather of the batch before its first wait.
 """
 import os
 import re
@@ -128,3 +131,13 @@ def test_token_major_batches_drain(asm):
     # the first batch's 16 row loads, a full drain, then the second batch's 16
     between = [d for d in drains if rows[15] < d < rows[16]]
     assert between, "no drain between the two batches"
+
+
+@pytest.mark.parametrize("layout,epi,kc", [(0, 1, -12), (0, 1, -4), (0, 0, 8), (1, 4, -4)])
+def test_half_idle_wave_issues_every_gather_first(asm, layout, epi, kc):
+    # vectors per thread 1, not exact (hidden 256, 768, ..., 7936)
+    k = body(asm, kernel_name(layout, False, epi, kc, 1, False))
+    loads = [m.start() for m in re.finditer(r"buffer_load_dwordx4 .* offen nt$", k, flags=re.M)]
+    assert len(loads) == abs(kc), len(loads)
+    first_wait = re.search(r"s_waitcnt vmcnt\(\d+\)", k)
+    assert first_wait is None or first_wait.start() > loads[-1]
