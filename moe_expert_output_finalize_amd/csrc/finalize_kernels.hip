@@ -153,7 +153,9 @@ __device__ __forceinline__ float dpp_mov(float v)
 // Sum of v over the workgroup, returned to every thread.  All threads of the
 // workgroup must call it (it contains a barrier when there are several waves).
 // Two sums in one kernel use different banks, so the second's LDS writes
-// cannot overtake a slower wave's reads of the first.
+// cannot overtake a slower wave's reads of the first.  PAIR: a one-wave
+// workgroup holding two tokens; each half of the wave gets its own sum.
+template <bool PAIR = false>
 __device__ __forceinline__ float block_sum(float v, int bank = 0)
 {
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
@@ -161,6 +163,13 @@ __device__ __forceinline__ float block_sum(float v, int bank = 0)
     v += dpp_mov<0x141>(v);   // row_half_mirror: 8-lane sums
     v += dpp_mov<0x140>(v);   // row_mirror: 16-lane sums
     const int iv = __builtin_bit_cast(int, v);
+    if constexpr (PAIR) {
+        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+        return (threadIdx.x & 32) ? hi : lo;
+    }
     float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
               __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)) +
               __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
@@ -189,22 +198,26 @@ __device__ __forceinline__ float lane_value(float v, int l)
 // ------------------------------------------------------------ kernel -----
 
 // What follows a token's FP32 routed sum `acc`: the epilogue EPI and the
-// stores of token t's output row(s).  gv holds the norm weight (or post
-// weight) vectors and rv the token's residual vectors, as the epilogue needs.
-// All threads of the workgroup call it (the norms contain a barrier).
-template <Epilogue EPI, int VPT, bool EXACT>
+// stores of the workgroup's output row(s), which start at token t_row and
+// span out_nv 16-byte vectors (one row, or a pair's two adjacent rows).  gv
+// holds the norm weight (or post weight) vectors and rv the token's residual
+// vectors, as the epilogue needs.  All threads of the workgroup call it (the
+// norms contain a barrier).
+template <Epilogue EPI, int VPT, bool EXACT, bool PAIR>
 __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (&gv)[VPT],
                                              const u32x4 (&rv)[VPT], const FinalizeArgs &a,
-                                             int64_t t, int lane, int team, int nv)
+                                             int64_t t_row, int out_nv, int lane, int team)
 {
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
     constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
                                    EPI == Epilogue::kResidualNorm;
+    const int nv = a.hidden >> 3;
     const __amdgpu_buffer_rsrc_t out_row =
-        row_resource(a.out + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
-    // Lanes past the row (teams with more threads than vectors) store
-    // outside the resource, which drops them.
+        row_resource(a.out + t_row * (int64_t)a.hidden, (uint32_t)out_nv * 16u);
+    // Lanes past the row (teams with more threads than vectors, the second
+    // half of a pair without a second token) store outside the resource,
+    // which drops them.
     auto store = [&](int i, const u32x4 &o) {
         store_out_vec(out_row, (uint32_t)(lane + i * team) * 16u, o);
     };
@@ -251,7 +264,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-            ss = block_sum(ss, 0);
+            ss = block_sum<PAIR>(ss, 0);
             const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
             for (int i = 0; i < VPT; ++i)
@@ -290,7 +303,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
         u32x4 nv2[VPT];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;
+            const int j = (PAIR ? (lane & 31) : lane) + i * team;
             nv2[i] = (u32x4){0u, 0u, 0u, 0u};
             if (a.gain2)
                 nv2[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain2)[j]
@@ -302,10 +315,10 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-        ss = block_sum(ss, 1);
+        ss = block_sum<PAIR>(ss, 1);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps2);
         const __amdgpu_buffer_rsrc_t out2_row =
-            row_resource(a.out2 + t * (int64_t)a.hidden, (uint32_t)nv * 16u);
+            row_resource(a.out2 + t_row * (int64_t)a.hidden, (uint32_t)out_nv * 16u);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             u32x4 o;
@@ -348,7 +361,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);   // idle vectors hold 0
-        ss = block_sum(ss);
+        ss = block_sum<PAIR>(ss);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -388,13 +401,23 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 // barrier per slot keeps each slot's loads W slots ahead of its FMAs instead
 // of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
 // starts at +0 never becomes -0.
-template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT>
-__global__ void __launch_bounds__(max_team(VPT))
+//
+// PAIR (hidden 256, whose 32 vectors fill half a wave, with at most 4
+// slots): a one-wave workgroup finalizes tokens 2b and 2b + 1 of the
+// launch, lanes 0-31 the first and 32-63 the second, each half with its own
+// slot metadata, rows and norm; their output rows are adjacent, so one
+// resource spans both.  A missing second token (an odd count) re-reads the
+// first token's metadata with every slot masked, and its stores fall
+// outside the resource.
+template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT, bool PAIR>
+__global__ void __launch_bounds__(PAIR ? kWave : max_team(VPT))
 finalize_kernel(const FinalizeArgs a)
 {
     constexpr bool kIdx = L == Layout::kIndexMap;
-    constexpr int KB = slots_in_flight(kIdx, KC, VPT);
-    constexpr bool kRoll = rolling(kIdx, KC, VPT);
+    static_assert(!PAIR || (VPT == 1 && EXACT && pair_kernel(KC)),
+                  "a pair is two tokens of 32 vectors and at most 4 slots in one wave");
+    constexpr int KB = PAIR ? pair_batch(KC) : slots_in_flight(kIdx, KC, VPT);
+    constexpr bool kRoll = !PAIR && rolling(kIdx, KC, VPT);
     constexpr int kSlotsMax = KC > 0 ? KC : -KC;
     static_assert(KB >= 1 && (kRoll || KC <= 0 || KC % KB == 0), "batches divide top-k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
@@ -403,8 +426,13 @@ finalize_kernel(const FinalizeArgs a)
     const int team = blockDim.x;
     const int lane = threadIdx.x;
     const int nv = a.hidden >> 3;
-    const int64_t t = a.token_base + blockIdx.x;
+    // The workgroup's first token; a pair's second token t0 + 1 exists when
+    // it is below num_tokens.  vl: this lane's vector within its token's row.
+    const int64_t t0 = a.token_base + (int64_t)blockIdx.x * (PAIR ? 2 : 1);
+    const bool has_b = PAIR && t0 + 1 < a.num_tokens;
+    const int64_t t = t0;
     const int64_t tk = t * top_k;
+    const int vl = PAIR ? (lane & 31) : lane;
 
     // The norm weight is shared by every token and stays cache resident;
     // fetch it first so its latency hides under the gather.
@@ -414,7 +442,7 @@ finalize_kernel(const FinalizeArgs a)
                           a.gain != nullptr;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;
+            const int j = vl + i * team;
             gv[i] = (u32x4){0u, 0u, 0u, 0u};
             if (have)
                 gv[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain)[j]
@@ -428,8 +456,12 @@ finalize_kernel(const FinalizeArgs a)
         const u32x4 *rr = reinterpret_cast<const u32x4 *>(a.residual + t * (int64_t)a.hidden);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;
-            rv[i] = EXACT ? load_row_vec(rr + j) : load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, nv, j);
+            const int j = lane + i * team;   // a pair's two rows are adjacent
+            if constexpr (PAIR)
+                rv[i] = load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, has_b ? 2 * nv : nv, j);
+            else
+                rv[i] = EXACT ? load_row_vec(rr + j)
+                              : load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, nv, j);
         }
     }
 
@@ -514,6 +546,71 @@ finalize_kernel(const FinalizeArgs a)
                 issue(s + W);
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else if constexpr (PAIR) {
+        // Two tokens per wave.  Both tokens' slot metadata is uniform
+        // (scalar loads); each slot's rows arrive through two buffer loads,
+        // one per token's row resource: the other half's lanes fall outside
+        // the 512-byte resource and read zeros, so the two results combine
+        // with an OR, and no lane branches.  An invalid slot, or a missing
+        // second token, gets an empty resource and weight 0.
+        const int64_t tk_b = (has_b ? t0 + 1 : t0) * top_k;
+        const int off_a = lane * 16;          // lanes 32-63: past token A's row
+        const int off_b = (lane ^ 32) * 16;   // lanes 0-31: past token B's row
+        const bool upper = lane >= 32;
+        const uint64_t rows = reinterpret_cast<uintptr_t>(a.rows);
+#pragma unroll
+        for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
+            if (KC < 0 && k0 >= top_k)
+                break;
+            u32x4 v[KB];
+            float w[KB];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int k = k0 + b;
+                const bool live = KC > 0 || k < top_k;
+                const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
+                bool ok_a, ok_b;
+                int64_t off_ra, off_rb;   // elements
+                float w_a = 1.0f, w_b = 1.0f;
+                if constexpr (kIdx) {
+                    const int32_t ia = a.idx[tk + kk], ib = a.idx[tk_b + kk];
+                    w_a = load_weight<W_BF16>(a.weights, tk + kk);
+                    w_b = load_weight<W_BF16>(a.weights, tk_b + kk);
+                    ok_a = live && ia >= 0 && (int64_t)ia < a.num_rows;
+                    ok_b = live && has_b && ib >= 0 && (int64_t)ib < a.num_rows;
+                    off_ra = (int64_t)ia * a.row_stride;
+                    off_rb = (int64_t)ib * a.row_stride;
+                } else if constexpr (L == Layout::kTokenMajor) {
+                    w_a = load_weight<W_BF16>(a.weights, tk + kk);
+                    w_b = load_weight<W_BF16>(a.weights, tk_b + kk);
+                    ok_a = live;
+                    ok_b = live && has_b;
+                    off_ra = (tk + kk) * (int64_t)a.hidden;
+                    off_rb = (tk_b + kk) * (int64_t)a.hidden;
+                } else {   // kDirect
+                    ok_a = live;
+                    ok_b = live && has_b;
+                    off_ra = t0 * a.row_stride;
+                    off_rb = (t0 + 1) * a.row_stride;
+                }
+                const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                    reinterpret_cast<void *>(rows + 2 * (uint64_t)off_ra), 0, ok_a ? nv * 16 : 0,
+                    kRawBufferWord3);
+                const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                    reinterpret_cast<void *>(rows + 2 * (uint64_t)off_rb), 0, ok_b ? nv * 16 : 0,
+                    kRawBufferWord3);
+                v[b] = __builtin_amdgcn_raw_buffer_load_b128(ra, off_a, 0, MF_ROW_LOAD_POLICY) |
+                       __builtin_amdgcn_raw_buffer_load_b128(rb, off_b, 0, MF_ROW_LOAD_POLICY);
+                w[b] = upper ? (ok_b ? w_b : 0.0f) : (ok_a ? w_a : 0.0f);
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[0][e] = __builtin_fmaf(w[b], elem(v[b], e), acc[0][e]);
+            if constexpr (kSlotsMax > KB)
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
     } else {
         // Batches of KB slots (one batch when every slot fits): uniform
         // per-slot data first (scalar loads, one wait), then every valid
@@ -582,7 +679,10 @@ finalize_kernel(const FinalizeArgs a)
         }
     }
 
-    finish_token<EPI, VPT, EXACT>(acc, gv, rv, a, t, lane, team, nv);
+    // A pair's two output rows are adjacent: one resource spans both, or
+    // only the first when there is no second token.
+    const int out_nv = has_b ? 2 * nv : nv;
+    finish_token<EPI, VPT, EXACT, PAIR>(acc, gv, rv, a, t0, out_nv, lane, team);
 }
 
 // ------------------------------------------------------------ dispatch ---
@@ -625,39 +725,52 @@ template <Layout L, bool W_BF16, Epilogue EPI, int KC>
 hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s)
 {
     const DeviceLimits d = device_limits();
-    const int64_t blocks =
-        residency_blocks(L == Layout::kIndexMap, a.hidden, p.slots, a.num_tokens, d.cus);
+    // A workgroup's rows in flight cover its p.tpw tokens.
+    const int64_t workgroups = (a.num_tokens + p.tpw - 1) / p.tpw;
+    const int64_t blocks = residency_blocks(L == Layout::kIndexMap, a.hidden * p.tpw, p.slots,
+                                            workgroups, d.cus);
     const size_t lds =
         (size_t)residency_lds(blocks, d.lds_per_cu, d.lds_per_block, kStaticLds);
     FinalizeArgs c = a;
     for (int64_t t0 = 0; t0 < a.num_tokens; t0 += p.max_tokens) {
         c.token_base = t0;
-        const dim3 grid((unsigned)std::min<int64_t>(p.max_tokens, a.num_tokens - t0));
+        const int64_t count = std::min<int64_t>(p.max_tokens, a.num_tokens - t0);
+        const dim3 grid((unsigned)((count + p.tpw - 1) / p.tpw));
         const dim3 block((unsigned)p.team);
+        if constexpr (pair_kernel(KC)) {
+            if (p.tpw == 2) {
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true, true>), grid,
+                                   block, lds, s, c);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return e;
+                continue;
+            }
+        }
         switch (p.vpt) {
         case 8:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 8))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true, false>), grid, block,
                                    lds, s, c);
             break;
         case 4:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 4))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true, false>), grid, block,
                                    lds, s, c);
             break;
         case 2:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 2))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true, false>), grid, block,
                                    lds, s, c);
             break;
         case 1:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 1))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true, false>), grid, block,
                                    lds, s, c);
             break;
         default:   // n odd: 32 (n + 1) threads, the last half wave idle
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 0))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false, false>), grid, block,
                                    lds, s, c);
             break;
         }

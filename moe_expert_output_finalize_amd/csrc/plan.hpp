@@ -41,6 +41,12 @@
 #ifndef MF_ROLL_WINDOW_VPT2
 #define MF_ROLL_WINDOW_VPT2 8
 #endif
+// Hidden 256 is 32 vectors, half of a 64-lane wave: at top-k up to 4 two
+// tokens share each wave, one per half (0: one token per workgroup with half
+// the wave idle).
+#ifndef MF_PAIR_HIDDEN_256
+#define MF_PAIR_HIDDEN_256 1
+#endif
 #ifndef MF_INFLIGHT_KB_PER_CU
 #define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
                                   // loads in flight total about this much per CU
@@ -177,14 +183,34 @@ constexpr bool vpt_possible(bool index_map, int kc, int vpt)
     return false;
 }
 
+// Whether kernels for slot-count argument kc pair tokens at hidden 256: a
+// token of 32 vectors and at most 4 slots moves 0.5-2 KiB, and one such
+// token per one-wave workgroup leaves the CU's 32 waves bound by latency
+// (measured, both layouts: top-k 1-2 17-25 % faster paired, top-k 4 2-6 %;
+// from top-k 6 on a token's rows fill the wave and pairing, with its two
+// loads per slot, was 1-9 % slower).
+constexpr bool pair_kernel(int kc) { return MF_PAIR_HIDDEN_256 && (kc < 0 ? -kc : kc) <= 4; }
+
+// Tokens one workgroup finalizes: two at hidden 256 with a paired kc (one
+// per half wave), else one.
+constexpr int tokens_per_workgroup(int hidden, int kc)
+{
+    return hidden == 256 && pair_kernel(kc) ? 2 : 1;
+}
+
+// Slots a paired workgroup has in flight: all of them (at most 4), each two
+// loads per lane, one per token, ORed.
+constexpr int pair_batch(int kc) { return kc < 0 ? -kc : kc; }
+
 // How one call is launched.
 struct LaunchPlan {
     int kc;               // slot-count template argument
     int vpt;              // 16-byte vectors per thread (0: one, last half wave idle)
-    int team;             // threads per workgroup (one token each)
-    int slots;            // slots whose rows a workgroup has in flight at once
-    bool exact;           // hidden / 8 == team * vpt
-    int64_t max_tokens;   // tokens per launch at most
+    int team;             // threads per workgroup
+    int tpw;              // tokens per workgroup (2: a pair at hidden 256)
+    int slots;            // slots per token whose rows a workgroup has in flight at once
+    bool exact;           // hidden / 8 == team * vpt (per token)
+    int64_t max_tokens;   // tokens per launch at most (a multiple of tpw)
 };
 
 constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int top_k)
@@ -192,13 +218,21 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
     LaunchPlan p{};
     const int n = hidden / 256;
     p.kc = direct ? 1 : kc_for_topk(top_k);
-    p.vpt = pick_vpt(index_map, n, p.kc);
-    p.exact = p.vpt > 0;
-    p.team = p.vpt > 0 ? 32 * n / p.vpt : 32 * n + 32;
+    p.tpw = tokens_per_workgroup(hidden, p.kc);
     const int kk = p.kc > 0 ? p.kc : top_k;
-    const int win = slots_in_flight(index_map, p.kc, p.vpt > 0 ? p.vpt : 1);
-    p.slots = kk < win ? kk : win;
-    p.max_tokens = kMaxThreadsPerLaunch / p.team;
+    if (p.tpw == 2) {   // one wave, lanes 0-31 the first token, 32-63 the second
+        p.vpt = 1;
+        p.exact = true;
+        p.team = kWave;
+        p.slots = kk < pair_batch(p.kc) ? kk : pair_batch(p.kc);
+    } else {
+        p.vpt = pick_vpt(index_map, n, p.kc);
+        p.exact = p.vpt > 0;
+        p.team = p.vpt > 0 ? 32 * n / p.vpt : 32 * n + 32;
+        const int win = slots_in_flight(index_map, p.kc, p.vpt > 0 ? p.vpt : 1);
+        p.slots = kk < win ? kk : win;
+    }
+    p.max_tokens = kMaxThreadsPerLaunch / p.team * p.tpw;
     return p;
 }
 

@@ -24,7 +24,7 @@ struct Record {
     int layout, epi;     // of the last call
     int64_t num_tokens;
     int hidden, top_k;
-    int kc, vpt, team;
+    int kc, vpt, team, tpw;
     int64_t launches;    // kernel launches the last call was split into
     int64_t max_tokens;  // tokens per launch at most
     int64_t blocks;      // workgroups per CU the launcher reserves LDS for, 256 CUs
@@ -81,13 +81,16 @@ int launch_finalize(const FinalizeArgs &a, Layout layout, Epilogue epi, void *st
     r.kc = p.kc;
     r.vpt = p.vpt;
     r.team = p.team;
+    r.tpw = p.tpw;
     r.max_tokens = p.max_tokens;
-    r.blocks = residency_blocks(idx_map, a.hidden, p.slots, a.num_tokens, 256);
+    r.blocks = residency_blocks(idx_map, a.hidden * p.tpw, p.slots,
+                                (a.num_tokens + p.tpw - 1) / p.tpw, 256);
     r.launches = 0;
     int64_t covered = 0;
     for (int64_t t0 = 0; t0 < a.num_tokens; t0 += p.max_tokens) {
         const int64_t n = a.num_tokens - t0 < p.max_tokens ? a.num_tokens - t0 : p.max_tokens;
-        if (n <= 0 || n * p.team > kMaxThreadsPerLaunch || t0 != covered)
+        if (n <= 0 || (n + p.tpw - 1) / p.tpw * p.team > kMaxThreadsPerLaunch || t0 != covered ||
+            (n < p.max_tokens ? false : n % p.tpw != 0))
             r.violations += 1;
         covered += n;
         r.launches += 1;
@@ -112,14 +115,14 @@ void mf_test_reset(void) { memset(&g_rec, 0, sizeof g_rec); }
 // Make the next launch fail with `code` (non-zero).
 void mf_test_fail_next_launch(int code) { g_rec.fail_next = code; }
 
-// The record, as 13 int64 values: calls, layout, epilogue, num_tokens, hidden,
-// top_k, kc, vpt, team, launches, max_tokens, blocks, violations.
+// The record, as 14 int64 values: calls, layout, epilogue, num_tokens, hidden,
+// top_k, kc, vpt, team, tpw, launches, max_tokens, blocks, violations.
 void mf_test_record(int64_t *out)
 {
     const Record &r = g_rec;
-    const int64_t v[13] = {r.calls,    r.layout, r.epi,      r.num_tokens, r.hidden,
-                           r.top_k,    r.kc,     r.vpt,      r.team,       r.launches,
-                           r.max_tokens, r.blocks, r.violations};
+    const int64_t v[14] = {r.calls,    r.layout,   r.epi,        r.num_tokens, r.hidden,
+                           r.top_k,    r.kc,       r.vpt,        r.team,       r.tpw,
+                           r.launches, r.max_tokens, r.blocks,   r.violations};
     memcpy(out, v, sizeof v);
 }
 

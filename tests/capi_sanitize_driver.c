@@ -140,10 +140,10 @@ int main(void)
         if (parse_args(kSigs[which].kinds, name + strlen(name) + 1, a) != 0)
             goto bad;
         int status = call(which, a);
-        int64_t rec[13];
+        int64_t rec[14];
         mf_test_record(rec);
         printf("%d", status);
-        for (int k = 0; k < 13; ++k)
+        for (int k = 0; k < 14; ++k)
             printf(" %lld", (long long)rec[k]);
         const char *msg = mf_last_error_message();
         printf(" %d\n", msg && msg[0] ? 1 : 0);

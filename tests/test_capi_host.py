@@ -97,10 +97,10 @@ def host():
 
 
 def record(lib) -> dict:
-    buf = (ctypes.c_int64 * 13)()
+    buf = (ctypes.c_int64 * 14)()
     lib.mf_test_record(buf)
     keys = ("calls", "layout", "epi", "num_tokens", "hidden", "top_k", "kc", "vpt", "team",
-            "launches", "max_tokens", "blocks", "violations")
+            "tpw", "launches", "max_tokens", "blocks", "violations")
     return dict(zip(keys, list(buf)))
 
 
@@ -128,7 +128,7 @@ def test_token_counts_beyond_one_launch_are_split(host, case):
     rec = record(host)
     assert rec["calls"] == 1 and rec["violations"] == 0
     assert rec["launches"] == launches
-    assert rec["max_tokens"] * rec["team"] <= 2 ** 31
+    assert rec["max_tokens"] // rec["tpw"] * rec["team"] <= 2 ** 31
     assert (rec["launches"] - 1) * rec["max_tokens"] < rec["num_tokens"]
     assert rec["launches"] * rec["max_tokens"] >= rec["num_tokens"]
 
@@ -146,25 +146,30 @@ def test_largest_token_count_at_every_hidden_size(host):
                 assert cc.ctypes_call(host, fn, over) == cc.OK, (fn, H, K)
                 rec = record(host)
                 assert rec["violations"] == 0 and rec["calls"] == 1, (fn, H, K, rec)
-                assert rec["max_tokens"] * rec["team"] <= 2 ** 31
+                assert rec["max_tokens"] // rec["tpw"] * rec["team"] <= 2 ** 31
 
 
-@pytest.mark.parametrize("fn,over,kc,vpt,team", [
-    ("moe_finalize_rmsnorm", dict(), 8, 1, 512),
-    ("moe_finalize_rmsnorm", dict(H=7168, stride=7168, K=32), -32, 2, 448),
-    ("moe_finalize_rmsnorm", dict(H=2048, stride=2048, K=12), -12, 1, 256),
-    ("moe_finalize_rmsnorm", dict(H=4096, K=2), -2, 4, 128),
-    ("moe_finalize", dict(H=256, stride=256, K=1), -2, 0, 64),
-    ("beam_moe_finalize", dict(), 8, 2, 448),
-    ("beam_moe_finalize", dict(K=17), -24, 2, 448),
-    ("mf_rmsnorm", dict(), 1, 2, 256),
+@pytest.mark.parametrize("fn,over,kc,vpt,team,tpw", [
+    ("moe_finalize_rmsnorm", dict(), 8, 1, 512, 1),
+    ("moe_finalize_rmsnorm", dict(H=7168, stride=7168, K=32), -32, 2, 448, 1),
+    ("moe_finalize_rmsnorm", dict(H=2048, stride=2048, K=12), -12, 1, 256, 1),
+    ("moe_finalize_rmsnorm", dict(H=4096, K=2), -2, 4, 128, 1),
+    ("moe_finalize", dict(H=256, stride=256, K=1), -2, 1, 64, 2),      # a pair per wave
+    ("moe_finalize", dict(H=768, stride=768, K=1), -2, 0, 128, 1),     # last half wave idle
+    ("beam_moe_finalize", dict(), 8, 2, 448, 1),
+    ("beam_moe_finalize", dict(K=17), -24, 2, 448, 1),
+    ("beam_moe_finalize", dict(H=256, K=3), -4, 1, 64, 2),
+    ("beam_moe_finalize", dict(H=256, K=6), -8, 0, 64, 1),       # top-k above 4: not paired
+    ("mf_rmsnorm", dict(), 1, 2, 256, 1),
+    ("mf_rmsnorm", dict(H=256, stride=256), 1, 1, 64, 2),
 ])
-def test_launch_plan(host, fn, over, kc, vpt, team):
-    """The kernel variant and team the launcher picks for a few shapes."""
+def test_launch_plan(host, fn, over, kc, vpt, team, tpw):
+    """The kernel variant, team and tokens per workgroup the launcher picks
+    for a few shapes."""
     host.mf_test_reset()
     assert cc.ctypes_call(host, fn, over) == cc.OK
     rec = record(host)
-    assert (rec["kc"], rec["vpt"], rec["team"]) == (kc, vpt, team), rec
+    assert (rec["kc"], rec["vpt"], rec["team"], rec["tpw"]) == (kc, vpt, team, tpw), rec
 
 
 # Workgroups per CU the launcher reserves LDS for on a 256-CU device: about

@@ -68,8 +68,8 @@ def test_capi_host_code_clean_under_asan_ubsan():
     assert len(out) == len(want)
     for line, (kind, fn, over, expect) in zip(out, want):
         v = [int(x) for x in line.split()]
-        status, rec, has_msg = v[0], v[1:14], v[14]
-        calls, launches, violations = rec[0], rec[9], rec[12]
+        status, rec, has_msg = v[0], v[1:15], v[15]
+        calls, launches, violations = rec[0], rec[10], rec[13]
         what = (kind, fn, over, line)
         assert violations == 0, what
         if kind == "status":

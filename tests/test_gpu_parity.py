@@ -212,19 +212,21 @@ def test_residual_norm_beam5_shape():
     (False, False, True, True, (1.5, -0.75)), (True, True, True, True, (1.0, 1.0)),
 ])
 def test_residual_norm_options(post, post_w, nxt, next_w, scales):
-    for hidden, K, scale in ((7168, 8, 2.5), (2048, 16, 1.0), (768, 3, 0.75), (8192, 1, 1.0)):
+    for hidden, K, scale in ((7168, 8, 2.5), (2048, 16, 1.0), (768, 3, 0.75), (8192, 1, 1.0),
+                             (256, 3, 1.0), (256, 16, 1.25)):
         args = residual_case(70 + hidden + K, 40, K, hidden, 33, post, post_w, nxt, next_w,
                              scales, scale)
         check_residual(*args, f"H={hidden} K={K} post={post} next={nxt} scales={scales}")
 
 
-def test_consumer_alone_matches_oracle():
+@pytest.mark.parametrize("T,H", [(50, 4096), (51, 256)])
+def test_consumer_alone_matches_oracle(T, H):
     """The consumer on its own.  Without a post-norm it is compared with the
     oracle directly.  With one, the post-normed y (within 1 ulp) is read back
     through a zero residual, the oracle checks y and the consumer applied to
-    the GPU's y, and the one-call result must equal the two-call one."""
-    rng = np.random.Generator(np.random.PCG64(90))
-    T, H = 50, 4096
+    the GPU's y, and the one-call result must equal the two-call one.  (At
+    hidden 256 two tokens share a wave; 51 leaves the last one alone.)"""
+    rng = np.random.Generator(np.random.PCG64(90 + H))
     x = wl.normal_bf16(rng, (T, H + 128))
     x[:, H:] = 0x7FC0
     res = wl.normal_bf16(rng, (T, H))
@@ -280,6 +282,35 @@ def test_one_round_residency_shapes(H, K, T):
     d = IndexMapOnDevice(c)
     assert_within_ulp(gpu_rmsnorm(d), oracle_rmsnorm(c), 1, NORM_MIN_EXACT, f"H={H} K={K} T={T}")
     assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"H={H} K={K} T={T}")
+
+
+# Hidden 256 at top-k up to 4: two tokens per wave, each half with its own
+# slots, masking and norm; odd counts leave the last token without a
+# partner.  Top-k 8, 13 and 32 run one token per workgroup beside them.
+@pytest.mark.parametrize("T", [1, 2, 3, 31, 2049])
+def test_pairs_at_hidden_256(T):
+    for K, wdt in ((1, "bf16"), (2, "fp32"), (3, "fp32"), (4, "bf16"), (8, "fp32"), (13, "bf16")):
+        c = wl.make_index_map_case(8000 + T + K, num_tokens=T, hidden=256, top_k=K,
+                                   num_rows=T * K + 9, row_stride=264, weights_dtype=wdt,
+                                   invalid_frac=0.1, poison=True, nan_rows_beyond=2)
+        d = IndexMapOnDevice(c)
+        what = f"T={T} K={K} {wdt}"
+        assert_bits_equal(gpu_finalize(d), oracle_finalize(c), what)
+        for wbn in (False, True):
+            assert_within_ulp(gpu_rmsnorm(d, weight_before_norm=wbn),
+                              oracle_rmsnorm(c, weight_before_norm=wbn), 1, NORM_MIN_EXACT,
+                              f"{what} wbn={wbn}")
+    for K, norm in ((1, True), (2, False), (3, False), (4, True), (16, True)):
+        b = wl.make_token_major_case(8100 + T + K, capacity=T + 2, top_k=K, hidden=256,
+                                     live_tokens=T, routed_scale=1.5,
+                                     post_eps=1e-6 if norm else None,
+                                     post_weight_std=0.05 if norm else None, poison_dead=True)
+        bd = TokenMajorOnDevice(b)
+        got, want = gpu_beam(bd), oracle_beam(b)
+        if norm:
+            assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"token major T={T} K={K}")
+        else:
+            assert_bits_equal(got, want, f"token major T={T} K={K}")
 
 
 def test_all_invalid_tokens_and_empty_row_matrix():

@@ -21,7 +21,9 @@ instruction:
   second batch's loads follow a full drain of the first's;
 - a team with more threads than vectors (hidden / 256 odd: the last half
   wave idle) reads its rows through buffer loads bounded at the row's end,
-  and issues every gather of the batch before its first wait.
+  and issues every gather of the batch before its first wait;
+- a pair (hidden 256, top-k up to 4: two tokens per wave) issues two buffer
+  loads per slot, one per token, all before its first wait, with no spills.
 """
 import os
 import re
@@ -59,12 +61,14 @@ def asm():
             return f.read()
 
 
-def kernel_name(layout, w_bf16, epi, kc, vpt, exact):
-    """Mangled name of finalize_kernel<Layout(layout), w_bf16, Epilogue(epi), kc, vpt, exact>."""
+def kernel_name(layout, w_bf16, epi, kc, vpt, exact, pair=False):
+    """Mangled name of
+    finalize_kernel<Layout(layout), w_bf16, Epilogue(epi), kc, vpt, exact, pair>."""
     num = (lambda v: f"n{-v}" if v < 0 else str(v))
     b = (lambda v: "1" if v else "0")
     return (f"_ZN2mf12_GLOBAL__N_115finalize_kernelILNS_6LayoutE{layout}ELb{b(w_bf16)}"
-            f"ELNS_8EpilogueE{epi}ELi{num(kc)}ELi{vpt}ELb{b(exact)}EEEvNS_12FinalizeArgsE")
+            f"ELNS_8EpilogueE{epi}ELi{num(kc)}ELi{vpt}ELb{b(exact)}ELb{b(pair)}"
+            f"EEEvNS_12FinalizeArgsE")
 
 
 def body(asm_text, name):
@@ -135,9 +139,20 @@ def test_token_major_batches_drain(asm):
 
 @pytest.mark.parametrize("layout,epi,kc", [(0, 1, -12), (0, 1, -4), (0, 0, 8), (1, 4, -4)])
 def test_half_idle_wave_issues_every_gather_first(asm, layout, epi, kc):
-    # vectors per thread 1, not exact (hidden 256, 768, ..., 7936)
+    # vectors per thread 1, not exact (hidden 768, 1280, ..., 7936)
     k = body(asm, kernel_name(layout, False, epi, kc, 1, False))
     loads = [m.start() for m in re.finditer(r"buffer_load_dwordx4 .* offen nt$", k, flags=re.M)]
     assert len(loads) == abs(kc), len(loads)
+    first_wait = re.search(r"s_waitcnt vmcnt\(\d+\)", k)
+    assert first_wait is None or first_wait.start() > loads[-1]
+
+
+@pytest.mark.parametrize("layout,epi,kc", [(0, 1, -4), (0, 0, -2), (1, 4, -4), (1, 5, -2), (2, 1, 1),
+                                           (2, 5, 1)])
+def test_pair_issues_both_tokens_gathers_first(asm, layout, epi, kc):
+    k = body(asm, kernel_name(layout, False, epi, kc, 1, True, pair=True))
+    loads = [m.start() for m in re.finditer(r"buffer_load_dwordx4 .* offen nt$", k, flags=re.M)]
+    # two per slot; the residual epilogue adds the pair's residual rows
+    assert len(loads) == 2 * abs(kc) + (1 if epi == 5 else 0), len(loads)
     first_wait = re.search(r"s_waitcnt vmcnt\(\d+\)", k)
     assert first_wait is None or first_wait.start() > loads[-1]
