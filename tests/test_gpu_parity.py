@@ -660,16 +660,19 @@ def _split_sample(T, boundary, seed):
                                      rng.integers(0, T, 1000)]))
 
 
-@pytest.mark.parametrize("H,K,team", [(256, 1, 64), (4096, 8, 512)])
-def test_index_map_split_into_launches_sampled(H, K, team):
+# (hidden, top-k, threads per workgroup, tokens per workgroup): hidden 256 at
+# top-k 1 pairs two tokens per wave, hidden 768 leaves half a wave idle.
+@pytest.mark.parametrize("H,K,team,tpw", [(256, 1, 64, 2), (768, 1, 128, 1), (4096, 8, 512, 1)])
+def test_index_map_split_into_launches_sampled(H, K, team, tpw):
     """A token count whose grid exceeds the 2^31 work-items one launch may
-    span (teams of `team` threads): the call runs as several launches, each
-    from its own first token.  Tokens on both sides of the first launch
+    span (teams of `team` threads, `tpw` tokens each): the call runs as
+    several launches, each from its own first token; an odd remainder leaves
+    the last pair one token.  Tokens on both sides of the first launch
     boundary, at both ends and spread over the range are compared with the
-    oracle (hidden 256 without a norm: bit-exact; hidden 4096 with the norm:
-    within 1 ulp)."""
-    per_launch = 2 ** 31 // team
-    T, R = per_launch + 3000, 4096
+    oracle (without a norm: bit-exact; hidden 4096 with the norm: within 1
+    ulp)."""
+    per_launch = 2 ** 31 // team * tpw
+    T, R = per_launch + 3001, 4096
     gen = torch.Generator(device="cuda")
     gen.manual_seed(90 + K)
     rows = torch.randn((R, H), generator=gen, device="cuda").to(torch.bfloat16)
@@ -698,14 +701,15 @@ def test_index_map_split_into_launches_sampled(H, K, team):
     torch.cuda.empty_cache()
 
 
-def test_token_major_split_into_launches_sampled():
-    """Token-major rows at hidden 256 (teams of 64) for 2^25 + 3000 live
-    tokens (17 GB of rows): two launches.  Sampled tokens around the
+@pytest.mark.parametrize("H,team,tpw", [(256, 64, 2), (768, 128, 1)])
+def test_token_major_split_into_launches_sampled(H, team, tpw):
+    """Token-major rows at top-k 1 for one launch's tokens plus 3001 (hidden
+    256: two tokens per wave, 2^26 + 3001 live tokens, 34 GB of rows; hidden
+    768: 2^24 + 3001, 26 GB): two launches.  Sampled tokens around the
     boundary and across the range are compared with the oracle bit for bit
     (no norm, routed_scale 1.25)."""
-    per_launch = 2 ** 31 // 64
-    C = per_launch + 3000
-    H = 256
+    per_launch = 2 ** 31 // team * tpw
+    C = per_launch + 3001
     gen = torch.Generator(device="cuda")
     gen.manual_seed(95)
     e = torch.empty((C, 1, H), dtype=torch.bfloat16, device="cuda")
