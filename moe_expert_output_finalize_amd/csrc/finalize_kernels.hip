@@ -104,6 +104,10 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 #endif
 }
 
+// A row of hidden 256 (32 vectors) of zeros, never written: a lane of a
+// multi-token wave reads it in place of a row it must not touch.
+__device__ __align__(16) u32x4 zero_row[32];
+
 // Buffer resource word 3 for raw (unformatted, unswizzled) access on gfx9.
 constexpr int kRawBufferWord3 = 0x00020000;
 
@@ -153,17 +157,23 @@ __device__ __forceinline__ float dpp_mov(float v)
 // Sum of v over the workgroup, returned to every thread.  All threads of the
 // workgroup must call it (it contains a barrier when there are several waves).
 // Two sums in one kernel use different banks, so the second's LDS writes
-// cannot overtake a slower wave's reads of the first.  PAIR: a one-wave
-// workgroup holding two tokens; each half of the wave gets its own sum.
-template <bool PAIR = false>
+// cannot overtake a slower wave's reads of the first.  TPW > 1: a one-wave
+// workgroup holding TPW tokens of 64 / TPW lanes each, and every lane gets
+// its own token's sum: with 8 or 4 tokens, the 8- or 16-lane sum every lane
+// holds after the DPP steps.
+template <int TPW = 1>
 __device__ __forceinline__ float block_sum(float v, int bank = 0)
 {
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
     v += dpp_mov<0x141>(v);   // row_half_mirror: 8-lane sums
+    if constexpr (TPW == 8)
+        return v;
     v += dpp_mov<0x140>(v);   // row_mirror: 16-lane sums
+    if constexpr (TPW == 4)
+        return v;
     const int iv = __builtin_bit_cast(int, v);
-    if constexpr (PAIR) {
+    if constexpr (TPW == 2) {
         const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
         const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
@@ -199,11 +209,11 @@ __device__ __forceinline__ float lane_value(float v, int l)
 
 // What follows a token's FP32 routed sum `acc`: the epilogue EPI and the
 // stores of the workgroup's output row(s), which start at token t_row and
-// span out_nv 16-byte vectors (one row, or a pair's two adjacent rows).  gv
+// span out_nv 16-byte vectors (one row, or TPW adjacent rows).  gv
 // holds the norm weight (or post weight) vectors and rv the token's residual
 // vectors, as the epilogue needs.  All threads of the workgroup call it (the
 // norms contain a barrier).
-template <Epilogue EPI, int VPT, bool EXACT, bool PAIR>
+template <Epilogue EPI, int VPT, bool EXACT, int TPW>
 __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (&gv)[VPT],
                                              const u32x4 (&rv)[VPT], const FinalizeArgs &a,
                                              int64_t t_row, int out_nv, int lane, int team)
@@ -213,14 +223,17 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
     constexpr bool kBeamRounding = EPI == Epilogue::kBeam || EPI == Epilogue::kBeamNorm ||
                                    EPI == Epilogue::kResidualNorm;
     const int nv = a.hidden >> 3;
+    // Vector i of this lane: column col(i) of its token's row, position st(i)
+    // among the workgroup's output vectors (TPW adjacent rows).
+    auto col = [&](int i) {
+        return TPW > 1 ? lane % (kWave / TPW) + (kWave / TPW) * i : lane + i * team;
+    };
+    auto st = [&](int i) { return TPW > 1 ? lane / (kWave / TPW) * nv + col(i) : col(i); };
     const __amdgpu_buffer_rsrc_t out_row =
         row_resource(a.out + t_row * (int64_t)a.hidden, (uint32_t)out_nv * 16u);
-    // Lanes past the row (teams with more threads than vectors, the second
-    // half of a pair without a second token) store outside the resource,
-    // which drops them.
-    auto store = [&](int i, const u32x4 &o) {
-        store_out_vec(out_row, (uint32_t)(lane + i * team) * 16u, o);
-    };
+    // Lanes past the row (teams with more threads than vectors, the lanes of
+    // tokens past the last) store outside the resource, which drops them.
+    auto store = [&](int i, const u32x4 &o) { store_out_vec(out_row, (uint32_t)st(i) * 16u, o); };
 
     if constexpr (EPI == Epilogue::kRound) {
 #pragma unroll
@@ -264,7 +277,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-            ss = block_sum<PAIR>(ss, 0);
+            ss = block_sum<TPW>(ss, 0);
             const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
             for (int i = 0; i < VPT; ++i)
@@ -303,7 +316,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
         u32x4 nv2[VPT];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = (PAIR ? (lane & 31) : lane) + i * team;
+            const int j = col(i);
             nv2[i] = (u32x4){0u, 0u, 0u, 0u};
             if (a.gain2)
                 nv2[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain2)[j]
@@ -315,7 +328,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-        ss = block_sum<PAIR>(ss, 1);
+        ss = block_sum<TPW>(ss, 1);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps2);
         const __amdgpu_buffer_rsrc_t out2_row =
             row_resource(a.out2 + t_row * (int64_t)a.hidden, (uint32_t)out_nv * 16u);
@@ -331,7 +344,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                 }
                 o[q] = pack_bf16x2(y0, y1);
             }
-            store_out_vec(out2_row, (uint32_t)(lane + i * team) * 16u, o);
+            store_out_vec(out2_row, (uint32_t)st(i) * 16u, o);
         }
         return;
     }
@@ -361,7 +374,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);   // idle vectors hold 0
-        ss = block_sum<PAIR>(ss);
+        ss = block_sum<TPW>(ss);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -402,49 +415,61 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 // of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
 // starts at +0 never becomes -0.
 //
-// PAIR (hidden 256, whose 32 vectors fill half a wave, with at most 4
-// slots): a one-wave workgroup finalizes tokens 2b and 2b + 1 of the
-// launch, lanes 0-31 the first and 32-63 the second, each half with its own
-// slot metadata, rows and norm; their output rows are adjacent, so one
-// resource spans both.  A missing second token (an odd count) re-reads the
-// first token's metadata with every slot masked, and its stores fall
-// outside the resource.
-template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT, bool PAIR>
-__global__ void __launch_bounds__(PAIR ? kWave : max_team(VPT))
+// TPW > 1 (hidden 256, whose 32 vectors fill half a wave, with at most 4
+// slots): a one-wave workgroup finalizes TPW consecutive tokens of the
+// launch, 64 / TPW lanes each, VPT = TPW / 2 vectors per lane; their output
+// rows are adjacent, so one resource spans them all.  Tokens past the last
+// gather nothing and their stores fall outside that resource.
+template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT, int TPW>
+__global__ void __launch_bounds__(TPW > 1 ? kWave : max_team(VPT))
 finalize_kernel(const FinalizeArgs a)
 {
     constexpr bool kIdx = L == Layout::kIndexMap;
-    static_assert(!PAIR || (VPT == 1 && EXACT && pair_kernel(KC)),
-                  "a pair is two tokens of 32 vectors and at most 4 slots in one wave");
-    constexpr int KB = PAIR ? pair_batch(KC) : slots_in_flight(kIdx, KC, VPT);
-    constexpr bool kRoll = !PAIR && rolling(kIdx, KC, VPT);
+    static_assert(TPW == 1 || (VPT * kWave == 32 * TPW && EXACT && wave_tokens(KC) == TPW),
+                  "TPW tokens of 32 vectors, at most 4 slots, in one wave");
+    constexpr int KB = TPW > 1 ? (KC > 0 ? KC : -KC) : slots_in_flight(kIdx, KC, VPT);
+    constexpr bool kRoll = TPW == 1 && rolling(kIdx, KC, VPT);
     constexpr int kSlotsMax = KC > 0 ? KC : -KC;
     static_assert(KB >= 1 && (kRoll || KC <= 0 || KC % KB == 0), "batches divide top-k");
     constexpr bool kNorm = EPI == Epilogue::kRmsNorm || EPI == Epilogue::kRmsNormWeightFirst ||
                            EPI == Epilogue::kBeamNorm;
+    // Lanes per token; with TPW > 1, lane l holds vectors l % LPT + LPT i of
+    // token l / LPT.
+    constexpr int LPT = kWave / TPW;
     const int top_k = KC > 0 ? KC : a.top_k;
     const int team = blockDim.x;
     const int lane = threadIdx.x;
     const int nv = a.hidden >> 3;
-    // The workgroup's first token; a pair's second token t0 + 1 exists when
-    // it is below num_tokens.  vl: this lane's vector within its token's row.
-    const int64_t t0 = a.token_base + (int64_t)blockIdx.x * (PAIR ? 2 : 1);
-    const bool has_b = PAIR && t0 + 1 < a.num_tokens;
+    // The workgroup's first token and how many of its TPW tokens exist.
+    // Multi-token waves read 4-16 bytes of slot metadata per token, so one
+    // cache line holds that of 8 or more workgroups: runs of consecutive
+    // token blocks go to one XCD (its own L2), which would otherwise fetch
+    // each line on all 8 (measured at top-k 1: 11 % more bytes read than
+    // the method moves on the index map, 5 % token major).
+    const unsigned blk = TPW > 1 ? xcd_run_block(blockIdx.x, gridDim.x, MF_XCD_RUN) : blockIdx.x;
+    const int64_t t0 = a.token_base + (int64_t)blk * TPW;
+    const int n_live = TPW == 1 || t0 + TPW <= a.num_tokens ? TPW : (int)(a.num_tokens - t0);
     const int64_t t = t0;
     const int64_t tk = t * top_k;
-    const int vl = PAIR ? (lane & 31) : lane;
+    auto col = [&](int i) { return TPW > 1 ? lane % LPT + LPT * i : lane + i * team; };
 
     // The norm weight is shared by every token and stays cache resident;
-    // fetch it first so its latency hides under the gather.
+    // fetch it first so its latency hides under the gather.  A multi-token
+    // wave reads an optional weight through a resource that is empty when
+    // the weight is absent: under a branch, the register copy that joins
+    // the two paths waits for the load before the first gather, which a
+    // wave of one-slot tokens, its whole life two round trips, cannot hide.
     u32x4 gv[VPT];
     if constexpr (kNorm || EPI == Epilogue::kResidualNorm) {
         const bool have = (EPI != Epilogue::kBeamNorm && EPI != Epilogue::kResidualNorm) ||
                           a.gain != nullptr;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = vl + i * team;
+            const int j = col(i);
             gv[i] = (u32x4){0u, 0u, 0u, 0u};
-            if (have)
+            if constexpr (TPW > 1)
+                gv[i] = load_vec_bounded<0>(a.gain, have ? nv : 0, j);
+            else if (have)
                 gv[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain)[j]
                               : load_vec_bounded<0>(a.gain, nv, j);
         }
@@ -456,9 +481,9 @@ finalize_kernel(const FinalizeArgs a)
         const u32x4 *rr = reinterpret_cast<const u32x4 *>(a.residual + t * (int64_t)a.hidden);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int j = lane + i * team;   // a pair's two rows are adjacent
-            if constexpr (PAIR)
-                rv[i] = load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, has_b ? 2 * nv : nv, j);
+            const int j = col(i);
+            if constexpr (TPW > 1)   // the workgroup's rows are adjacent
+                rv[i] = load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, n_live * nv, lane / LPT * nv + j);
             else
                 rv[i] = EXACT ? load_row_vec(rr + j)
                               : load_vec_bounded<MF_ROW_LOAD_POLICY>(rr, nv, j);
@@ -546,71 +571,78 @@ finalize_kernel(const FinalizeArgs a)
                 issue(s + W);
             __builtin_amdgcn_sched_barrier(0);
         }
-    } else if constexpr (PAIR) {
-        // Two tokens per wave.  Both tokens' slot metadata is uniform
-        // (scalar loads); each slot's rows arrive through two buffer loads,
-        // one per token's row resource: the other half's lanes fall outside
-        // the 512-byte resource and read zeros, so the two results combine
-        // with an OR, and no lane branches.  An invalid slot, or a missing
-        // second token, gets an empty resource and weight 0.
-        const int64_t tk_b = (has_b ? t0 + 1 : t0) * top_k;
-        const int off_a = lane * 16;          // lanes 32-63: past token A's row
-        const int off_b = (lane ^ 32) * 16;   // lanes 0-31: past token B's row
-        const bool upper = lane >= 32;
-        const uint64_t rows = reinterpret_cast<uintptr_t>(a.rows);
+    } else if constexpr (TPW > 1) {
+        // Every lane gathers its own token's rows through a per-lane
+        // address.  Slot metadata is uniform per token (scalar loads) and
+        // each lane picks its token's.  Three phases, in this order so that
+        // no wait stands between the row loads and their issue: the index
+        // map's row indices; every row load; the weights.  A lane whose slot
+        // is invalid or past a run-time top-k, or whose token is past the
+        // last, reads the zero row instead, with weight 0, so every load is
+        // unconditional.  A dead token's metadata reads are those of t0.
+        const int q = lane / LPT;
+        const bool live_q = q < n_live;
+        auto slot = [&](int u, int k) {   // metadata position of token t0 + u, slot k
+            const int64_t tu = u < n_live ? t0 + u : t0;
+            return tu * top_k + (KC > 0 ? k : (k < top_k ? k : top_k - 1));
+        };
+        // Each lane keeps its own token's value as the uniform values of the
+        // TPW tokens arrive (selected into a register, never an array the
+        // compiler could place in LDS).
+        int32_t ik[kSlotsMax] = {};
+        if constexpr (kIdx) {
 #pragma unroll
-        for (int k0 = 0; k0 < kSlotsMax; k0 += KB) {
-            if (KC < 0 && k0 >= top_k)
-                break;
-            u32x4 v[KB];
-            float w[KB];
+            for (int k = 0; k < kSlotsMax; ++k)
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                const int k = k0 + b;
-                const bool live = KC > 0 || k < top_k;
-                const int kk = KC > 0 ? k : (k < top_k ? k : top_k - 1);
-                bool ok_a, ok_b;
-                int64_t off_ra, off_rb;   // elements
-                float w_a = 1.0f, w_b = 1.0f;
-                if constexpr (kIdx) {
-                    const int32_t ia = a.idx[tk + kk], ib = a.idx[tk_b + kk];
-                    w_a = load_weight<W_BF16>(a.weights, tk + kk);
-                    w_b = load_weight<W_BF16>(a.weights, tk_b + kk);
-                    ok_a = live && ia >= 0 && (int64_t)ia < a.num_rows;
-                    ok_b = live && has_b && ib >= 0 && (int64_t)ib < a.num_rows;
-                    off_ra = (int64_t)ia * a.row_stride;
-                    off_rb = (int64_t)ib * a.row_stride;
-                } else if constexpr (L == Layout::kTokenMajor) {
-                    w_a = load_weight<W_BF16>(a.weights, tk + kk);
-                    w_b = load_weight<W_BF16>(a.weights, tk_b + kk);
-                    ok_a = live;
-                    ok_b = live && has_b;
-                    off_ra = (tk + kk) * (int64_t)a.hidden;
-                    off_rb = (tk_b + kk) * (int64_t)a.hidden;
-                } else {   // kDirect
-                    ok_a = live;
-                    ok_b = live && has_b;
-                    off_ra = t0 * a.row_stride;
-                    off_rb = (t0 + 1) * a.row_stride;
+                for (int u = 0; u < TPW; ++u) {
+                    const int32_t x = a.idx[slot(u, k)];
+                    ik[k] = u == 0 || q == u ? x : ik[k];
                 }
-                const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-                    reinterpret_cast<void *>(rows + 2 * (uint64_t)off_ra), 0, ok_a ? nv * 16 : 0,
-                    kRawBufferWord3);
-                const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                    reinterpret_cast<void *>(rows + 2 * (uint64_t)off_rb), 0, ok_b ? nv * 16 : 0,
-                    kRawBufferWord3);
-                v[b] = __builtin_amdgcn_raw_buffer_load_b128(ra, off_a, 0, MF_ROW_LOAD_POLICY) |
-                       __builtin_amdgcn_raw_buffer_load_b128(rb, off_b, 0, MF_ROW_LOAD_POLICY);
-                w[b] = upper ? (ok_b ? w_b : 0.0f) : (ok_a ? w_a : 0.0f);
-            }
+        }
+        const int64_t tq = live_q ? t0 + q : t0;
+        bool ok[kSlotsMax];
+        u32x4 v[kSlotsMax][VPT];
 #pragma unroll
-            for (int b = 0; b < KB; ++b)
+        for (int k = 0; k < kSlotsMax; ++k) {
+            ok[k] = live_q && (KC > 0 || k < top_k);
+            int64_t off;   // elements
+            if constexpr (kIdx) {
+                ok[k] = ok[k] && ik[k] >= 0 && (int64_t)ik[k] < a.num_rows;
+                off = (int64_t)ik[k] * a.row_stride;
+            } else if constexpr (L == Layout::kTokenMajor) {
+                off = (tq * top_k + k) * (int64_t)a.hidden;
+            } else {   // kDirect
+                off = tq * a.row_stride;
+            }
+            const u32x4 *src =
+                (ok[k] ? reinterpret_cast<const u32x4 *>(a.rows + off) : zero_row) + lane % LPT;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
+                v[k][i] = load_row_vec(src + LPT * i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float w[kSlotsMax];
+#pragma unroll
+        for (int k = 0; k < kSlotsMax; ++k) {
+            w[k] = 1.0f;
+            if constexpr (L != Layout::kDirect)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const float x = load_weight<W_BF16>(a.weights, slot(u, k));
+                    w[k] = u == 0 || q == u ? x : w[k];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kSlotsMax; ++k)
+            w[k] = ok[k] ? w[k] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < kSlotsMax; ++k)
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    acc[0][e] = __builtin_fmaf(w[b], elem(v[b], e), acc[0][e]);
-            if constexpr (kSlotsMax > KB)
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        }
+                    acc[i][e] = __builtin_fmaf(w[k], elem(v[k][i], e), acc[i][e]);
     } else {
         // Batches of KB slots (one batch when every slot fits): uniform
         // per-slot data first (scalar loads, one wait), then every valid
@@ -679,10 +711,9 @@ finalize_kernel(const FinalizeArgs a)
         }
     }
 
-    // A pair's two output rows are adjacent: one resource spans both, or
-    // only the first when there is no second token.
-    const int out_nv = has_b ? 2 * nv : nv;
-    finish_token<EPI, VPT, EXACT, PAIR>(acc, gv, rv, a, t0, out_nv, lane, team);
+    // The workgroup's output rows are adjacent: one resource spans those of
+    // its live tokens.
+    finish_token<EPI, VPT, EXACT, TPW>(acc, gv, rv, a, t0, n_live * nv, lane, team);
 }
 
 // ------------------------------------------------------------ dispatch ---
@@ -737,40 +768,45 @@ hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s
         const int64_t count = std::min<int64_t>(p.max_tokens, a.num_tokens - t0);
         const dim3 grid((unsigned)((count + p.tpw - 1) / p.tpw));
         const dim3 block((unsigned)p.team);
-        if constexpr (pair_kernel(KC)) {
-            if (p.tpw == 2) {
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true, true>), grid,
-                                   block, lds, s, c);
+        if constexpr (wave_tokens(KC) > 1) {
+            if (p.tpw > 1) {
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, wave_tokens(KC) / 2, true,
+                                                    wave_tokens(KC)>),
+                                   grid, block, lds, s, c);
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess)
                     return e;
                 continue;
             }
         }
+        // A routed call reaches slot count 1 only at hidden 256, whose
+        // multi-token kernel ran above: no one-token kernel exists for it.
+        if constexpr (KC == 1 && L != Layout::kDirect)
+            return hipErrorInvalidValue;
         switch (p.vpt) {
         case 8:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 8))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 8, true, 1>), grid, block,
                                    lds, s, c);
             break;
         case 4:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 4))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 4, true, 1>), grid, block,
                                    lds, s, c);
             break;
         case 2:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 2))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 2, true, 1>), grid, block,
                                    lds, s, c);
             break;
         case 1:
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 1))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, true, 1>), grid, block,
                                    lds, s, c);
             break;
         default:   // n odd: 32 (n + 1) threads, the last half wave idle
             if constexpr (vpt_possible(L == Layout::kIndexMap, KC, 0))
-                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false, false>), grid, block,
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, 1, false, 1>), grid, block,
                                    lds, s, c);
             break;
         }
@@ -788,6 +824,10 @@ hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
 {
     const LaunchPlan p = plan_launch(L == Layout::kIndexMap, false, a.hidden, a.top_k);
     switch (p.kc) {
+    case 1:   // top-k 1 at hidden 256: several tokens per wave
+        if constexpr (wave_tokens(1) > 1)
+            return launch_plan<L, W_BF16, EPI, 1>(a, p, s);
+        return hipErrorInvalidValue;
     case 8:
         return launch_plan<L, W_BF16, EPI, 8>(a, p, s);
     case 16:

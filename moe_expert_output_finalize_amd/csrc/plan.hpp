@@ -41,11 +41,12 @@
 #ifndef MF_ROLL_WINDOW_VPT2
 #define MF_ROLL_WINDOW_VPT2 8
 #endif
-// Hidden 256 is 32 vectors, half of a 64-lane wave: at top-k up to 4 two
-// tokens share each wave, one per half (0: one token per workgroup with half
-// the wave idle).
-#ifndef MF_PAIR_HIDDEN_256
-#define MF_PAIR_HIDDEN_256 1
+// Hidden 256 is 32 vectors, half of a 64-lane wave: at top-k up to 4
+// several tokens share each one-wave workgroup, as many (2, 4 or 8) as keep
+// tokens x slots at most this (0: one token per workgroup with half the
+// wave idle).
+#ifndef MF_WAVE_TOKEN_SLOTS
+#define MF_WAVE_TOKEN_SLOTS 4
 #endif
 #ifndef MF_INFLIGHT_KB_PER_CU
 #define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
@@ -56,10 +57,19 @@
 #ifndef MF_ONE_ROUND_MAX_BLOCKS
 #define MF_ONE_ROUND_MAX_BLOCKS 8
 #endif
+// Multi-token waves (hidden 256) hand runs of this many consecutive
+// workgroups to one XCD, so that a cache line of slot metadata is fetched
+// into one XCD's L2 rather than every XCD's (0 or 1: workgroup b finalizes
+// token block b).
+#ifndef MF_XCD_RUN
+#define MF_XCD_RUN 32
+#endif
 
 namespace mf {
 
 constexpr int kWave = 64;
+// XCDs of an MI355X; the dispatcher deals workgroup b of a grid to XCD b % 8.
+constexpr unsigned kXcds = 8;
 constexpr int kMaxTopK = 32;   // the entry points reject larger top-k
 constexpr int kMaxWaves = 16;
 // Work-items one launch may span.  The dispatch packet counts the grid in
@@ -183,31 +193,49 @@ constexpr bool vpt_possible(bool index_map, int kc, int vpt)
     return false;
 }
 
-// Whether kernels for slot-count argument kc pair tokens at hidden 256: a
-// token of 32 vectors and at most 4 slots moves 0.5-2 KiB, and one such
-// token per one-wave workgroup leaves the CU's 32 waves bound by latency
-// (measured, both layouts: top-k 1-2 17-25 % faster paired, top-k 4 2-6 %;
-// from top-k 6 on a token's rows fill the wave and pairing, with its two
-// loads per slot, was 1-9 % slower).
-constexpr bool pair_kernel(int kc) { return MF_PAIR_HIDDEN_256 && (kc < 0 ? -kc : kc) <= 4; }
-
-// Tokens one workgroup finalizes: two at hidden 256 with a paired kc (one
-// per half wave), else one.
-constexpr int tokens_per_workgroup(int hidden, int kc)
+// The token block workgroup b of an n-workgroup grid finalizes when runs of
+// `run` consecutive blocks go to one XCD: XCD x = b % kXcds receives its
+// i-th workgroup (i = b / kXcds) from run i / run, and runs are interleaved
+// over the XCDs in block order.  The grid's last partial group of
+// kXcds * run workgroups keeps b, so the map is a bijection on [0, n) for
+// any n (and any XCD count: only the locality depends on it).
+constexpr unsigned xcd_run_block(unsigned b, unsigned n, unsigned run)
 {
-    return hidden == 256 && pair_kernel(kc) ? 2 : 1;
+    const unsigned span = kXcds * run;
+    if (run <= 1 || b >= n / span * span)
+        return b;
+    const unsigned x = b % kXcds, i = b / kXcds;
+    return (i / run * kXcds + x) * run + i % run;
 }
 
-// Slots a paired workgroup has in flight: all of them (at most 4), each two
-// loads per lane, one per token, ORed.
-constexpr int pair_batch(int kc) { return kc < 0 ? -kc : kc; }
+// Tokens a one-wave workgroup of kernels for slot-count argument kc
+// finalizes at hidden 256: a token of 32 vectors and at most 4 slots moves
+// 0.5-2 KiB, and one such token per wave leaves the CU's 32 waves bound by
+// latency.  The largest of 8, 4, 2 with tokens x slots within
+// MF_WAVE_TOKEN_SLOTS (at least 2), for kc up to 4 slots; else 1.
+constexpr int wave_tokens(int kc)
+{
+    const int k = kc < 0 ? -kc : kc;
+    if (MF_WAVE_TOKEN_SLOTS <= 0 || k > 4)
+        return 1;
+    int t = 8;
+    while (t > 2 && t * k > MF_WAVE_TOKEN_SLOTS)
+        t /= 2;
+    return t;
+}
+
+// Tokens one workgroup finalizes: wave_tokens(kc) at hidden 256, else one.
+constexpr int tokens_per_workgroup(int hidden, int kc)
+{
+    return hidden == 256 ? wave_tokens(kc) : 1;
+}
 
 // How one call is launched.
 struct LaunchPlan {
     int kc;               // slot-count template argument
     int vpt;              // 16-byte vectors per thread (0: one, last half wave idle)
     int team;             // threads per workgroup
-    int tpw;              // tokens per workgroup (2: a pair at hidden 256)
+    int tpw;              // tokens per workgroup (2, 4 or 8: one wave at hidden 256)
     int slots;            // slots per token whose rows a workgroup has in flight at once
     bool exact;           // hidden / 8 == team * vpt (per token)
     int64_t max_tokens;   // tokens per launch at most (a multiple of tpw)
@@ -218,13 +246,17 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
     LaunchPlan p{};
     const int n = hidden / 256;
     p.kc = direct ? 1 : kc_for_topk(top_k);
+    // Top-k 1 at hidden 256 runs slot count 1 when that packs more tokens
+    // per wave than the run-time kernel for 1-2 slots.
+    if (hidden == 256 && top_k == 1 && wave_tokens(1) > wave_tokens(p.kc))
+        p.kc = 1;
     p.tpw = tokens_per_workgroup(hidden, p.kc);
     const int kk = p.kc > 0 ? p.kc : top_k;
-    if (p.tpw == 2) {   // one wave, lanes 0-31 the first token, 32-63 the second
-        p.vpt = 1;
+    if (p.tpw > 1) {   // one wave, 64 / tpw lanes per token, all slots at once
+        p.vpt = 32 * p.tpw / kWave;
         p.exact = true;
         p.team = kWave;
-        p.slots = kk < pair_batch(p.kc) ? kk : pair_batch(p.kc);
+        p.slots = kk;
     } else {
         p.vpt = pick_vpt(index_map, n, p.kc);
         p.exact = p.vpt > 0;

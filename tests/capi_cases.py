@@ -130,17 +130,20 @@ CASES = (
 # Token counts whose launches must be split: (entry point, overrides,
 # expected number of launches).  The work-items of one launch are capped at
 # 2^31; the team is 512 threads at hidden 4096 on the index map (one vector
-# per thread), 64 at hidden 256 (one wave holding two tokens, so 2^26 tokens
-# per launch), 256 at token-major hidden 4096 (two vectors per thread), 448
+# per thread), 64 at hidden 256 (one wave holding four tokens at top-k 1, so
+# 2^27 tokens per launch, and two at top-k 2, 2^26), 256 at token-major
+# hidden 4096 (two vectors per thread), 448
 # at 7168, and 512 for the standalone norm at hidden 8192 (two vectors per
 # thread).
 SPLIT_CASES = [
     ("moe_finalize_rmsnorm", dict(T=4_194_304), 1),
     ("moe_finalize_rmsnorm", dict(T=4_194_305), 2),
     ("moe_finalize_rmsnorm", dict(T=8_388_609), 3),
-    ("moe_finalize", dict(T=INT32_MAX, H=256, stride=256, K=1), 32),
-    ("moe_finalize", dict(T=67_108_864, H=256, stride=256, K=1), 1),
-    ("moe_finalize", dict(T=67_108_865, H=256, stride=256, K=1), 2),
+    ("moe_finalize", dict(T=INT32_MAX, H=256, stride=256, K=1), 16),
+    ("moe_finalize", dict(T=134_217_728, H=256, stride=256, K=1), 1),
+    ("moe_finalize", dict(T=134_217_729, H=256, stride=256, K=1), 2),
+    ("moe_finalize", dict(T=67_108_864, H=256, stride=256, K=2), 1),
+    ("moe_finalize", dict(T=67_108_865, H=256, stride=256, K=2), 2),
     ("beam_moe_finalize", dict(cap=INT32_MAX, wrows=INT32_MAX, live=INT32_MAX, H=4096), 256),
     ("beam_moe_finalize", dict(cap=10_000_000, wrows=10_000_000, live=4_793_491), 2),
     ("mf_rmsnorm", dict(T=INT32_MAX, H=8192, stride=8192), 512),

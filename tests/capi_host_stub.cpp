@@ -126,4 +126,11 @@ void mf_test_record(int64_t *out)
     memcpy(out, v, sizeof v);
 }
 
+// Token block of workgroup b in an n-workgroup grid of a multi-token-wave
+// kernel, with the library's own run length (the map the kernels use).
+unsigned mf_test_xcd_run_block(unsigned b, unsigned n)
+{
+    return mf::xcd_run_block(b, n, MF_XCD_RUN);
+}
+
 }  // extern "C"

@@ -154,14 +154,16 @@ def test_largest_token_count_at_every_hidden_size(host):
     ("moe_finalize_rmsnorm", dict(H=7168, stride=7168, K=32), -32, 2, 448, 1),
     ("moe_finalize_rmsnorm", dict(H=2048, stride=2048, K=12), -12, 1, 256, 1),
     ("moe_finalize_rmsnorm", dict(H=4096, K=2), -2, 4, 128, 1),
-    ("moe_finalize", dict(H=256, stride=256, K=1), -2, 1, 64, 2),      # a pair per wave
+    ("moe_finalize", dict(H=256, stride=256, K=1), 1, 2, 64, 4),       # four tokens per wave
+    ("moe_finalize", dict(H=256, stride=256, K=2), -2, 1, 64, 2),      # two tokens per wave
     ("moe_finalize", dict(H=768, stride=768, K=1), -2, 0, 128, 1),     # last half wave idle
     ("beam_moe_finalize", dict(), 8, 2, 448, 1),
     ("beam_moe_finalize", dict(K=17), -24, 2, 448, 1),
     ("beam_moe_finalize", dict(H=256, K=3), -4, 1, 64, 2),
-    ("beam_moe_finalize", dict(H=256, K=6), -8, 0, 64, 1),       # top-k above 4: not paired
+    ("beam_moe_finalize", dict(H=256, K=1), 1, 2, 64, 4),
+    ("beam_moe_finalize", dict(H=256, K=6), -8, 0, 64, 1),       # top-k above 4: one token
     ("mf_rmsnorm", dict(), 1, 2, 256, 1),
-    ("mf_rmsnorm", dict(H=256, stride=256), 1, 1, 64, 2),
+    ("mf_rmsnorm", dict(H=256, stride=256), 1, 2, 64, 4),
 ])
 def test_launch_plan(host, fn, over, kc, vpt, team, tpw):
     """The kernel variant, team and tokens per workgroup the launcher picks
@@ -228,3 +230,22 @@ def test_c_driver_links_against_the_library():
     assert os.path.exists(driver), "run __graft_entry__.build() first"
     r = subprocess.run([driver], capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "usage:" in r.stderr
+
+
+@pytest.mark.parametrize("n", [1, 7, 63, 255, 256, 257, 1000, 4096 + 17, 32768])
+def test_xcd_runs_are_a_permutation_of_token_blocks(host, n):
+    """Multi-token-wave kernels hand runs of consecutive token blocks to one
+    XCD (workgroup b runs on XCD b % 8): every block of the grid is still
+    finalized exactly once, and in the full groups XCD x's successive
+    workgroups take consecutive blocks."""
+    host.mf_test_xcd_run_block.argtypes = [ctypes.c_uint, ctypes.c_uint]
+    host.mf_test_xcd_run_block.restype = ctypes.c_uint
+    m = [host.mf_test_xcd_run_block(b, n) for b in range(n)]
+    assert sorted(m) == list(range(n))
+    run = 32
+    full = n // (8 * run) * (8 * run)
+    for b in range(full - 8):
+        if (b // 8) % run != run - 1:
+            assert m[b + 8] == m[b] + 1, (b, m[b], m[b + 8])
+    assert m[full:] == list(range(full, n))
+

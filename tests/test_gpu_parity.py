@@ -213,7 +213,7 @@ def test_residual_norm_beam5_shape():
 ])
 def test_residual_norm_options(post, post_w, nxt, next_w, scales):
     for hidden, K, scale in ((7168, 8, 2.5), (2048, 16, 1.0), (768, 3, 0.75), (8192, 1, 1.0),
-                             (256, 3, 1.0), (256, 16, 1.25)):
+                             (256, 1, 1.5), (256, 3, 1.0), (256, 16, 1.25)):
         args = residual_case(70 + hidden + K, 40, K, hidden, 33, post, post_w, nxt, next_w,
                              scales, scale)
         check_residual(*args, f"H={hidden} K={K} post={post} next={nxt} scales={scales}")
@@ -225,7 +225,7 @@ def test_consumer_alone_matches_oracle(T, H):
     oracle directly.  With one, the post-normed y (within 1 ulp) is read back
     through a zero residual, the oracle checks y and the consumer applied to
     the GPU's y, and the one-call result must equal the two-call one.  (At
-    hidden 256 two tokens share a wave; 51 leaves the last one alone.)"""
+    hidden 256 four tokens share a wave; 51 leaves the last wave three.)"""
     rng = np.random.Generator(np.random.PCG64(90 + H))
     x = wl.normal_bf16(rng, (T, H + 128))
     x[:, H:] = 0x7FC0
@@ -284,11 +284,12 @@ def test_one_round_residency_shapes(H, K, T):
     assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"H={H} K={K} T={T}")
 
 
-# Hidden 256 at top-k up to 4: two tokens per wave, each half with its own
-# slots, masking and norm; odd counts leave the last token without a
-# partner.  Top-k 8, 13 and 32 run one token per workgroup beside them.
-@pytest.mark.parametrize("T", [1, 2, 3, 31, 2049])
-def test_pairs_at_hidden_256(T):
+# Hidden 256 at top-k up to 4: several tokens per wave (four at top-k 1, two
+# at top-k 2-4), each lane group with its own slots, masking and norm; token
+# counts that are not a multiple leave the last wave partly empty.  Top-k 8
+# and 13 run one token per workgroup beside them.
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 6, 31, 2049])
+def test_several_tokens_per_wave_at_hidden_256(T):
     for K, wdt in ((1, "bf16"), (2, "fp32"), (3, "fp32"), (4, "bf16"), (8, "fp32"), (13, "bf16")):
         c = wl.make_index_map_case(8000 + T + K, num_tokens=T, hidden=256, top_k=K,
                                    num_rows=T * K + 9, row_stride=264, weights_dtype=wdt,
@@ -660,17 +661,19 @@ def _split_sample(T, boundary, seed):
                                      rng.integers(0, T, 1000)]))
 
 
-# (hidden, top-k, threads per workgroup, tokens per workgroup): hidden 256 at
-# top-k 1 pairs two tokens per wave, hidden 768 leaves half a wave idle.
-@pytest.mark.parametrize("H,K,team,tpw", [(256, 1, 64, 2), (768, 1, 128, 1), (4096, 8, 512, 1)])
+# (hidden, top-k, threads per workgroup, tokens per workgroup): hidden 256
+# holds four tokens per wave at top-k 1 and two at top-k 2, hidden 768 leaves
+# half a wave idle.
+@pytest.mark.parametrize("H,K,team,tpw", [(256, 1, 64, 4), (256, 2, 64, 2), (768, 1, 128, 1),
+                                          (4096, 8, 512, 1)])
 def test_index_map_split_into_launches_sampled(H, K, team, tpw):
     """A token count whose grid exceeds the 2^31 work-items one launch may
     span (teams of `team` threads, `tpw` tokens each): the call runs as
-    several launches, each from its own first token; an odd remainder leaves
-    the last pair one token.  Tokens on both sides of the first launch
-    boundary, at both ends and spread over the range are compared with the
-    oracle (without a norm: bit-exact; hidden 4096 with the norm: within 1
-    ulp)."""
+    several launches, each from its own first token; the remainder of 3001
+    leaves the last multi-token wave one token.  Tokens on both sides of the
+    first launch boundary, at both ends and spread over the range are
+    compared with the oracle (top-k 1 without a norm: bit-exact; otherwise
+    with the norm: within 1 ulp)."""
     per_launch = 2 ** 31 // team * tpw
     T, R = per_launch + 3001, 4096
     gen = torch.Generator(device="cuda")
@@ -701,10 +704,10 @@ def test_index_map_split_into_launches_sampled(H, K, team, tpw):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("H,team,tpw", [(256, 64, 2), (768, 128, 1)])
+@pytest.mark.parametrize("H,team,tpw", [(256, 64, 4), (768, 128, 1)])
 def test_token_major_split_into_launches_sampled(H, team, tpw):
     """Token-major rows at top-k 1 for one launch's tokens plus 3001 (hidden
-    256: two tokens per wave, 2^26 + 3001 live tokens, 34 GB of rows; hidden
+    256: four tokens per wave, 2^27 + 3001 live tokens, 69 GB of rows; hidden
     768: 2^24 + 3001, 26 GB): two launches.  Sampled tokens around the
     boundary and across the range are compared with the oracle bit for bit
     (no norm, routed_scale 1.25)."""

@@ -22,8 +22,10 @@ instruction:
 - a team with more threads than vectors (hidden / 256 odd: the last half
   wave idle) reads its rows through buffer loads bounded at the row's end,
   and issues every gather of the batch before its first wait;
-- a pair (hidden 256, top-k up to 4: two tokens per wave) issues two buffer
-  loads per slot, one per token, all before its first wait, with no spills.
+- a wave holding several tokens (hidden 256, top-k up to 4: four tokens at
+  top-k 1, two at 2-4) issues every slot's row loads, one 16-byte load per
+  vector per lane, before its first wait, keeps no per-token array in LDS,
+  and has no spills.
 """
 import os
 import re
@@ -61,13 +63,13 @@ def asm():
             return f.read()
 
 
-def kernel_name(layout, w_bf16, epi, kc, vpt, exact, pair=False):
+def kernel_name(layout, w_bf16, epi, kc, vpt, exact, tpw=1):
     """Mangled name of
-    finalize_kernel<Layout(layout), w_bf16, Epilogue(epi), kc, vpt, exact, pair>."""
+    finalize_kernel<Layout(layout), w_bf16, Epilogue(epi), kc, vpt, exact, tpw>."""
     num = (lambda v: f"n{-v}" if v < 0 else str(v))
     b = (lambda v: "1" if v else "0")
     return (f"_ZN2mf12_GLOBAL__N_115finalize_kernelILNS_6LayoutE{layout}ELb{b(w_bf16)}"
-            f"ELNS_8EpilogueE{epi}ELi{num(kc)}ELi{vpt}ELb{b(exact)}ELb{b(pair)}"
+            f"ELNS_8EpilogueE{epi}ELi{num(kc)}ELi{vpt}ELb{b(exact)}ELi{tpw}"
             f"EEEvNS_12FinalizeArgsE")
 
 
@@ -147,12 +149,17 @@ def test_half_idle_wave_issues_every_gather_first(asm, layout, epi, kc):
     assert first_wait is None or first_wait.start() > loads[-1]
 
 
-@pytest.mark.parametrize("layout,epi,kc", [(0, 1, -4), (0, 0, -2), (1, 4, -4), (1, 5, -2), (2, 1, 1),
-                                           (2, 5, 1)])
-def test_pair_issues_both_tokens_gathers_first(asm, layout, epi, kc):
-    k = body(asm, kernel_name(layout, False, epi, kc, 1, True, pair=True))
-    loads = [m.start() for m in re.finditer(r"buffer_load_dwordx4 .* offen nt$", k, flags=re.M)]
-    # two per slot; the residual epilogue adds the pair's residual rows
-    assert len(loads) == 2 * abs(kc) + (1 if epi == 5 else 0), len(loads)
+@pytest.mark.parametrize("layout,epi,kc,tpw", [(0, 1, 1, 4), (0, 0, -2, 2), (0, 1, -4, 2),
+                                               (1, 4, 1, 4), (1, 5, -2, 2), (2, 1, 1, 4),
+                                               (2, 5, 1, 4)])
+def test_multi_token_wave_issues_every_gather_first(asm, layout, epi, kc, tpw):
+    name = kernel_name(layout, False, epi, kc, tpw // 2, True, tpw)
+    k = body(asm, name)
+    loads = [m.start() for m in re.finditer(r"global_load_dwordx4 .* nt$", k, flags=re.M)]
+    # each lane: tpw / 2 vectors of its token's row per slot
+    assert len(loads) == abs(kc) * (tpw // 2), len(loads)
     first_wait = re.search(r"s_waitcnt vmcnt\(\d+\)", k)
     assert first_wait is None or first_wait.start() > loads[-1]
+    # the per-token slot metadata stays in registers (an array the compiler
+    # placed in LDS would show as static LDS beyond the norm's 128 bytes)
+    assert metadata(asm)[name].get("group_segment_fixed_size", 0) <= 128
