@@ -147,6 +147,10 @@ SPLIT_CASES = [
     ("beam_moe_finalize", dict(cap=INT32_MAX, wrows=INT32_MAX, live=INT32_MAX, H=4096), 256),
     ("beam_moe_finalize", dict(cap=10_000_000, wrows=10_000_000, live=4_793_491), 2),
     ("mf_rmsnorm", dict(T=INT32_MAX, H=8192, stride=8192), 512),
+    ("mf_rmsnorm", dict(T=INT32_MAX, H=256, stride=256), 16),
+    ("beam_norm_residual_norm", dict(T=INT32_MAX, H=256, stride=256), 16),
+    ("beam_moe_finalize_norm_residual_norm",
+     dict(cap=INT32_MAX, wrows=INT32_MAX, T=INT32_MAX, H=256, K=2), 32),
 ]
 
 
