@@ -41,7 +41,7 @@
 #ifndef MF_ROLL_WINDOW_VPT2
 #define MF_ROLL_WINDOW_VPT2 8
 #endif
-// Hidden 256 is 32 vectors, half of a 64-lane wave: at top-k up to 4
+// Hidden 256 is 32 vectors, half of a 64-lane wave: at small top-k
 // several tokens share each one-wave workgroup, as many (2, 4 or 8) as keep
 // tokens x slots at most this (0: one token per workgroup with half the
 // wave idle).
@@ -212,11 +212,15 @@ constexpr unsigned xcd_run_block(unsigned b, unsigned n, unsigned run)
 // finalizes at hidden 256: a token of 32 vectors and at most 4 slots moves
 // 0.5-2 KiB, and one such token per wave leaves the CU's 32 waves bound by
 // latency.  The largest of 8, 4, 2 with tokens x slots within
-// MF_WAVE_TOKEN_SLOTS (at least 2), for kc up to 4 slots; else 1.
+// MF_WAVE_TOKEN_SLOTS (at least 2), for kc up to 4 slots and for the
+// run-time kernel of up to 8 (top-k 5-7, where one token per wave leaves
+// half of it idle: index map 3-4 % faster with two); else 1 (the
+// compile-time 8 was 1.3 % slower with two, and above 8 slots every slot in
+// flight at once loses to the rolling window).
 constexpr int wave_tokens(int kc)
 {
     const int k = kc < 0 ? -kc : kc;
-    if (MF_WAVE_TOKEN_SLOTS <= 0 || k > 4)
+    if (MF_WAVE_TOKEN_SLOTS <= 0 || (k > 4 && kc != -8))
         return 1;
     int t = 8;
     while (t > 2 && t * k > MF_WAVE_TOKEN_SLOTS)

@@ -161,7 +161,9 @@ def test_largest_token_count_at_every_hidden_size(host):
     ("beam_moe_finalize", dict(K=17), -24, 2, 448, 1),
     ("beam_moe_finalize", dict(H=256, K=3), -4, 1, 64, 2),
     ("beam_moe_finalize", dict(H=256, K=1), 1, 2, 64, 4),
-    ("beam_moe_finalize", dict(H=256, K=6), -8, 0, 64, 1),       # top-k above 4: one token
+    ("beam_moe_finalize", dict(H=256, K=6), -8, 1, 64, 2),       # run-time 8 slots: two
+    ("beam_moe_finalize", dict(H=256, K=8), 8, 0, 64, 1),        # compile-time 8: one token
+    ("moe_finalize", dict(H=256, stride=256, K=12), -12, 0, 64, 1),
     ("mf_rmsnorm", dict(), 1, 2, 256, 1),
     ("mf_rmsnorm", dict(H=256, stride=256), 1, 2, 64, 4),
 ])

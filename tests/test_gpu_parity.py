@@ -284,13 +284,14 @@ def test_one_round_residency_shapes(H, K, T):
     assert_bits_equal(gpu_finalize(d), oracle_finalize(c), f"H={H} K={K} T={T}")
 
 
-# Hidden 256 at top-k up to 4: several tokens per wave (four at top-k 1, two
-# at top-k 2-4), each lane group with its own slots, masking and norm; token
+# Hidden 256 at top-k up to 7: several tokens per wave (four at top-k 1, two
+# at top-k 2-7), each lane group with its own slots, masking and norm; token
 # counts that are not a multiple leave the last wave partly empty.  Top-k 8
 # and 13 run one token per workgroup beside them.
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 6, 31, 2049])
 def test_several_tokens_per_wave_at_hidden_256(T):
-    for K, wdt in ((1, "bf16"), (2, "fp32"), (3, "fp32"), (4, "bf16"), (8, "fp32"), (13, "bf16")):
+    for K, wdt in ((1, "bf16"), (2, "fp32"), (3, "fp32"), (4, "bf16"), (6, "fp32"), (7, "bf16"),
+                   (8, "fp32"), (13, "bf16")):
         c = wl.make_index_map_case(8000 + T + K, num_tokens=T, hidden=256, top_k=K,
                                    num_rows=T * K + 9, row_stride=264, weights_dtype=wdt,
                                    invalid_frac=0.1, poison=True, nan_rows_beyond=2)
@@ -301,7 +302,8 @@ def test_several_tokens_per_wave_at_hidden_256(T):
             assert_within_ulp(gpu_rmsnorm(d, weight_before_norm=wbn),
                               oracle_rmsnorm(c, weight_before_norm=wbn), 1, NORM_MIN_EXACT,
                               f"{what} wbn={wbn}")
-    for K, norm in ((1, True), (2, False), (3, False), (4, True), (16, True)):
+    for K, norm in ((1, True), (2, False), (3, False), (4, True), (5, False), (7, True),
+                    (16, True)):
         b = wl.make_token_major_case(8100 + T + K, capacity=T + 2, top_k=K, hidden=256,
                                      live_tokens=T, routed_scale=1.5,
                                      post_eps=1e-6 if norm else None,

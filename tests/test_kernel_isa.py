@@ -22,8 +22,8 @@ instruction:
 - a team with more threads than vectors (hidden / 256 odd: the last half
   wave idle) reads its rows through buffer loads bounded at the row's end,
   and issues every gather of the batch before its first wait;
-- a wave holding several tokens (hidden 256, top-k up to 4: four tokens at
-  top-k 1, two at 2-4) issues every slot's row loads, one 16-byte load per
+- a wave holding several tokens (hidden 256: four tokens at top-k 1, two
+  at top-k 2-7) issues every slot's row loads, one 16-byte load per
   vector per lane, before its first wait, keeps no per-token array in LDS,
   and has no spills.
 """
@@ -150,6 +150,7 @@ def test_half_idle_wave_issues_every_gather_first(asm, layout, epi, kc):
 
 
 @pytest.mark.parametrize("layout,epi,kc,tpw", [(0, 1, 1, 4), (0, 0, -2, 2), (0, 1, -4, 2),
+                                               (0, 1, -8, 2), (1, 4, -8, 2),
                                                (1, 4, 1, 4), (1, 5, -2, 2), (2, 1, 1, 4),
                                                (2, 5, 1, 4)])
 def test_multi_token_wave_issues_every_gather_first(asm, layout, epi, kc, tpw):
