@@ -33,7 +33,7 @@
  *    (num_tokens, 4096)].  A call whose grid would span more than 2^31
  *    work-items (one workgroup of up to 1024 threads per token, or one
  *    64-thread wave per four tokens at hidden 256 and top-k 1, per two at
- *    top-k 2-7) runs as
+ *    top-k 2-7 and at hidden 512 and top-k 1) runs as
  *    several launches on `stream`, in token order; the split is invisible
  *    to the caller.
  *  - The output must not overlap any input.  Calls on different streams may

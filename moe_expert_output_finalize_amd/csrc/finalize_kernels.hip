@@ -104,9 +104,9 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 #endif
 }
 
-// A row of hidden 256 (32 vectors) of zeros, never written: a lane of a
+// A row of hidden 512 (64 vectors) of zeros, never written: a lane of a
 // multi-token wave reads it in place of a row it must not touch.
-__device__ __align__(16) u32x4 zero_row[32];
+__device__ __align__(16) u32x4 zero_row[64];
 
 // Buffer resource word 3 for raw (unformatted, unswizzled) access on gfx9.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -415,18 +415,20 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
 // of all at the top.  fma(0, 0, acc) == acc bit for bit, since a sum that
 // starts at +0 never becomes -0.
 //
-// TPW > 1 (hidden 256, whose 32 vectors fill half a wave, with at most 4
-// slots): a one-wave workgroup finalizes TPW consecutive tokens of the
-// launch, 64 / TPW lanes each, VPT = TPW / 2 vectors per lane; their output
-// rows are adjacent, so one resource spans them all.  Tokens past the last
-// gather nothing and their stores fall outside that resource.
+// TPW > 1 (hidden 256, whose 32 vectors fill half a wave, up to top-k 7;
+// hidden 512 at top-k 1): a one-wave workgroup finalizes TPW consecutive
+// tokens of the launch, 64 / TPW lanes each, VPT = hidden / 8 / (64 / TPW)
+// vectors per lane; their output rows are adjacent, so one resource spans
+// them all.  Tokens past the last gather nothing and their stores fall
+// outside that resource.
 template <Layout L, bool W_BF16, Epilogue EPI, int KC, int VPT, bool EXACT, int TPW>
 __global__ void __launch_bounds__(TPW > 1 ? kWave : max_team(VPT))
 finalize_kernel(const FinalizeArgs a)
 {
     constexpr bool kIdx = L == Layout::kIndexMap;
-    static_assert(TPW == 1 || (VPT * kWave == 32 * TPW && EXACT && wave_tokens(KC) == TPW),
-                  "TPW tokens of 32 vectors, at most 4 slots, in one wave");
+    static_assert(TPW == 1 || (EXACT && ((VPT * kWave == 32 * TPW && wave_tokens(KC) == TPW) ||
+                                         (VPT * kWave == 64 * TPW && KC == 1 && TPW == 2))),
+                  "TPW tokens of 32 vectors (hidden 256) or two of 64 (hidden 512) in one wave");
     constexpr int KB = TPW > 1 ? (KC > 0 ? KC : -KC) : slots_in_flight(kIdx, KC, VPT);
     constexpr bool kRoll = TPW == 1 && rolling(kIdx, KC, VPT);
     constexpr int kSlotsMax = KC > 0 ? KC : -KC;
@@ -769,7 +771,7 @@ hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s
         const dim3 grid((unsigned)((count + p.tpw - 1) / p.tpw));
         const dim3 block((unsigned)p.team);
         if constexpr (wave_tokens(KC) > 1) {
-            if (p.tpw > 1) {
+            if (p.tpw == wave_tokens(KC) && p.vpt == wave_tokens(KC) / 2) {   // hidden 256
                 hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, KC, wave_tokens(KC) / 2, true,
                                                     wave_tokens(KC)>),
                                    grid, block, lds, s, c);
@@ -779,8 +781,19 @@ hipError_t launch_plan(const FinalizeArgs &a, const LaunchPlan &p, hipStream_t s
                 continue;
             }
         }
-        // A routed call reaches slot count 1 only at hidden 256, whose
-        // multi-token kernel ran above: no one-token kernel exists for it.
+        if constexpr (KC == 1 && MF_WAVE_TOKENS_512) {
+            if (p.tpw == 2 && p.vpt == 2) {   // hidden 512, two tokens per wave
+                hipLaunchKernelGGL((finalize_kernel<L, W_BF16, EPI, 1, 2, true, 2>), grid, block,
+                                   lds, s, c);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return e;
+                continue;
+            }
+        }
+        // A routed call reaches slot count 1 only at hidden 256 and 512,
+        // whose multi-token kernels ran above: no one-token kernel exists
+        // for it.
         if constexpr (KC == 1 && L != Layout::kDirect)
             return hipErrorInvalidValue;
         switch (p.vpt) {
@@ -824,8 +837,8 @@ hipError_t launch_topk(const FinalizeArgs &a, hipStream_t s)
 {
     const LaunchPlan p = plan_launch(L == Layout::kIndexMap, false, a.hidden, a.top_k);
     switch (p.kc) {
-    case 1:   // top-k 1 at hidden 256: several tokens per wave
-        if constexpr (wave_tokens(1) > 1)
+    case 1:   // top-k 1 at hidden 256 and 512: several tokens per wave
+        if constexpr (wave_tokens(1) > 1 || MF_WAVE_TOKENS_512)
             return launch_plan<L, W_BF16, EPI, 1>(a, p, s);
         return hipErrorInvalidValue;
     case 8:

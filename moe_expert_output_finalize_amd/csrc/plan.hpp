@@ -48,6 +48,11 @@
 #ifndef MF_WAVE_TOKEN_SLOTS
 #define MF_WAVE_TOKEN_SLOTS 4
 #endif
+// Hidden 512 (64 vectors, a whole wave) at top-k 1: two tokens per wave,
+// 32 lanes of two vectors each (0: one token per wave).
+#ifndef MF_WAVE_TOKENS_512
+#define MF_WAVE_TOKENS_512 1
+#endif
 #ifndef MF_INFLIGHT_KB_PER_CU
 #define MF_INFLIGHT_KB_PER_CU 128 // > 0: cap resident workgroups so that their row
                                   // loads in flight total about this much per CU
@@ -228,10 +233,14 @@ constexpr int wave_tokens(int kc)
     return t;
 }
 
-// Tokens one workgroup finalizes: wave_tokens(kc) at hidden 256, else one.
+// Tokens one workgroup finalizes: wave_tokens(kc) at hidden 256, two at
+// hidden 512 with one slot (a token's single row is 1 KiB, and one token per
+// wave leaves too few bytes in flight behind the index round trip), else one.
 constexpr int tokens_per_workgroup(int hidden, int kc)
 {
-    return hidden == 256 ? wave_tokens(kc) : 1;
+    return hidden == 256                           ? wave_tokens(kc)
+           : hidden == 512 && kc == 1 && MF_WAVE_TOKENS_512 ? 2
+                                                   : 1;
 }
 
 // How one call is launched.
@@ -251,13 +260,15 @@ constexpr LaunchPlan plan_launch(bool index_map, bool direct, int hidden, int to
     const int n = hidden / 256;
     p.kc = direct ? 1 : kc_for_topk(top_k);
     // Top-k 1 at hidden 256 runs slot count 1 when that packs more tokens
-    // per wave than the run-time kernel for 1-2 slots.
-    if (hidden == 256 && top_k == 1 && wave_tokens(1) > wave_tokens(p.kc))
+    // per wave than the run-time kernel for 1-2 slots; at hidden 512 slot
+    // count 1 holds two tokens per wave.
+    if (top_k == 1 && ((hidden == 256 && wave_tokens(1) > wave_tokens(p.kc)) ||
+                       (hidden == 512 && MF_WAVE_TOKENS_512)))
         p.kc = 1;
     p.tpw = tokens_per_workgroup(hidden, p.kc);
     const int kk = p.kc > 0 ? p.kc : top_k;
     if (p.tpw > 1) {   // one wave, 64 / tpw lanes per token, all slots at once
-        p.vpt = 32 * p.tpw / kWave;
+        p.vpt = 32 * n * p.tpw / kWave;
         p.exact = true;
         p.team = kWave;
         p.slots = kk;

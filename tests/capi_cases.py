@@ -144,6 +144,8 @@ SPLIT_CASES = [
     ("moe_finalize", dict(T=134_217_729, H=256, stride=256, K=1), 2),
     ("moe_finalize", dict(T=67_108_864, H=256, stride=256, K=2), 1),
     ("moe_finalize", dict(T=67_108_865, H=256, stride=256, K=2), 2),
+    ("moe_finalize", dict(T=INT32_MAX, H=512, stride=512, K=1), 32),
+    ("moe_finalize", dict(T=67_108_865, H=512, stride=512, K=1), 2),
     ("beam_moe_finalize", dict(cap=INT32_MAX, wrows=INT32_MAX, live=INT32_MAX, H=4096), 256),
     ("beam_moe_finalize", dict(cap=10_000_000, wrows=10_000_000, live=4_793_491), 2),
     ("mf_rmsnorm", dict(T=INT32_MAX, H=8192, stride=8192), 512),

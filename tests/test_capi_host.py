@@ -156,6 +156,10 @@ def test_largest_token_count_at_every_hidden_size(host):
     ("moe_finalize_rmsnorm", dict(H=4096, K=2), -2, 4, 128, 1),
     ("moe_finalize", dict(H=256, stride=256, K=1), 1, 2, 64, 4),       # four tokens per wave
     ("moe_finalize", dict(H=256, stride=256, K=2), -2, 1, 64, 2),      # two tokens per wave
+    ("moe_finalize", dict(H=512, stride=512, K=1), 1, 2, 64, 2),       # two tokens of 64 vectors
+    ("moe_finalize", dict(H=512, stride=512, K=2), -2, 1, 64, 1),      # one token per wave
+    ("beam_moe_finalize", dict(H=512, K=1), 1, 2, 64, 2),
+    ("mf_rmsnorm", dict(H=512, stride=512), 1, 2, 64, 2),
     ("moe_finalize", dict(H=768, stride=768, K=1), -2, 0, 128, 1),     # last half wave idle
     ("beam_moe_finalize", dict(), 8, 2, 448, 1),
     ("beam_moe_finalize", dict(K=17), -24, 2, 448, 1),

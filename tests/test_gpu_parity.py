@@ -219,13 +219,14 @@ def test_residual_norm_options(post, post_w, nxt, next_w, scales):
         check_residual(*args, f"H={hidden} K={K} post={post} next={nxt} scales={scales}")
 
 
-@pytest.mark.parametrize("T,H", [(50, 4096), (51, 256)])
+@pytest.mark.parametrize("T,H", [(50, 4096), (51, 256), (51, 512)])
 def test_consumer_alone_matches_oracle(T, H):
     """The consumer on its own.  Without a post-norm it is compared with the
     oracle directly.  With one, the post-normed y (within 1 ulp) is read back
     through a zero residual, the oracle checks y and the consumer applied to
     the GPU's y, and the one-call result must equal the two-call one.  (At
-    hidden 256 four tokens share a wave; 51 leaves the last wave three.)"""
+    hidden 256 four tokens share a wave, at 512 two; 51 leaves the last
+    wave three and one.)"""
     rng = np.random.Generator(np.random.PCG64(90 + H))
     x = wl.normal_bf16(rng, (T, H + 128))
     x[:, H:] = 0x7FC0
@@ -314,6 +315,34 @@ def test_several_tokens_per_wave_at_hidden_256(T):
             assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"token major T={T} K={K}")
         else:
             assert_bits_equal(got, want, f"token major T={T} K={K}")
+
+
+# Hidden 512 at top-k 1: two tokens per wave (32 lanes of two vectors
+# each); top-k 2 runs one token per wave beside it.
+@pytest.mark.parametrize("T", [1, 2, 3, 31, 2049])
+def test_two_tokens_per_wave_at_hidden_512(T):
+    for K, wdt in ((1, "bf16"), (1, "fp32"), (2, "fp32")):
+        c = wl.make_index_map_case(8200 + T + K, num_tokens=T, hidden=512, top_k=K,
+                                   num_rows=T * K + 9, row_stride=520, weights_dtype=wdt,
+                                   invalid_frac=0.1, poison=True, nan_rows_beyond=2)
+        d = IndexMapOnDevice(c)
+        what = f"H=512 T={T} K={K} {wdt}"
+        assert_bits_equal(gpu_finalize(d), oracle_finalize(c), what)
+        for wbn in (False, True):
+            assert_within_ulp(gpu_rmsnorm(d, weight_before_norm=wbn),
+                              oracle_rmsnorm(c, weight_before_norm=wbn), 1, NORM_MIN_EXACT,
+                              f"{what} wbn={wbn}")
+    for norm in (False, True):
+        b = wl.make_token_major_case(8300 + T, capacity=T + 2, top_k=1, hidden=512,
+                                     live_tokens=T, routed_scale=1.5,
+                                     post_eps=1e-6 if norm else None,
+                                     post_weight_std=0.05 if norm else None, poison_dead=True)
+        bd = TokenMajorOnDevice(b)
+        got, want = gpu_beam(bd), oracle_beam(b)
+        if norm:
+            assert_within_ulp(got, want, 1, NORM_MIN_EXACT, f"token major H=512 T={T}")
+        else:
+            assert_bits_equal(got, want, f"token major H=512 T={T}")
 
 
 def test_all_invalid_tokens_and_empty_row_matrix():
@@ -619,14 +648,14 @@ def test_token_major_offsets_beyond_4_gib_sampled():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("H", [1024, 256])
+@pytest.mark.parametrize("H", [1024, 256, 512])
 def test_negative_zero_passes_through_direct_rows(H):
     """Rows read directly (the standalone norm and the residual consumer)
     keep -0: the sum starts from -0, so fma(1, -0, -0) stays -0 where a +0
     start would turn it into +0.  Elements whose oracle value is a zero must
     match it bit for bit, sign included (the ulp comparison counts +0 and -0
     as equal); the rest within 1 ulp.  Hidden 256 runs four tokens per wave
-    (9 tokens: the last wave holds one)."""
+    and 512 two (9 tokens: the last wave holds one)."""
     rng = np.random.Generator(np.random.PCG64(97))
     T = 9
     x = wl.normal_bf16(rng, (T, H))
@@ -666,10 +695,10 @@ def _split_sample(T, boundary, seed):
 
 
 # (hidden, top-k, threads per workgroup, tokens per workgroup): hidden 256
-# holds four tokens per wave at top-k 1 and two at top-k 2, hidden 768 leaves
-# half a wave idle.
-@pytest.mark.parametrize("H,K,team,tpw", [(256, 1, 64, 4), (256, 2, 64, 2), (768, 1, 128, 1),
-                                          (4096, 8, 512, 1)])
+# holds four tokens per wave at top-k 1 and two at top-k 2, hidden 512 two at
+# top-k 1, hidden 768 leaves half a wave idle.
+@pytest.mark.parametrize("H,K,team,tpw", [(256, 1, 64, 4), (256, 2, 64, 2), (512, 1, 64, 2),
+                                          (768, 1, 128, 1), (4096, 8, 512, 1)])
 def test_index_map_split_into_launches_sampled(H, K, team, tpw):
     """A token count whose grid exceeds the 2^31 work-items one launch may
     span (teams of `team` threads, `tpw` tokens each): the call runs as

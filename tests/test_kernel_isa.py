@@ -23,7 +23,7 @@ instruction:
   wave idle) reads its rows through buffer loads bounded at the row's end,
   and issues every gather of the batch before its first wait;
 - a wave holding several tokens (hidden 256: four tokens at top-k 1, two
-  at top-k 2-7) issues every slot's row loads, one 16-byte load per
+  at top-k 2-7; hidden 512 at top-k 1: two) issues every slot's row loads, one 16-byte load per
   vector per lane, before its first wait, keeps no per-token array in LDS,
   and has no spills.
 """
@@ -149,16 +149,18 @@ def test_half_idle_wave_issues_every_gather_first(asm, layout, epi, kc):
     assert first_wait is None or first_wait.start() > loads[-1]
 
 
-@pytest.mark.parametrize("layout,epi,kc,tpw", [(0, 1, 1, 4), (0, 0, -2, 2), (0, 1, -4, 2),
-                                               (0, 1, -8, 2), (1, 4, -8, 2),
-                                               (1, 4, 1, 4), (1, 5, -2, 2), (2, 1, 1, 4),
-                                               (2, 5, 1, 4)])
-def test_multi_token_wave_issues_every_gather_first(asm, layout, epi, kc, tpw):
-    name = kernel_name(layout, False, epi, kc, tpw // 2, True, tpw)
+# (layout, epilogue, slot count, vectors per lane, tokens per wave): hidden
+# 256 holds 4 tokens of 2 vectors per lane or 2 of 1; hidden 512 2 of 2.
+@pytest.mark.parametrize("layout,epi,kc,vpt,tpw", [
+    (0, 1, 1, 2, 4), (0, 0, -2, 1, 2), (0, 1, -4, 1, 2), (0, 1, -8, 1, 2), (1, 4, -8, 1, 2),
+    (1, 4, 1, 2, 4), (1, 5, -2, 1, 2), (2, 1, 1, 2, 4), (2, 5, 1, 2, 4),
+    (0, 1, 1, 2, 2), (0, 0, 1, 2, 2), (1, 4, 1, 2, 2), (2, 1, 1, 2, 2), (2, 5, 1, 2, 2)])
+def test_multi_token_wave_issues_every_gather_first(asm, layout, epi, kc, vpt, tpw):
+    name = kernel_name(layout, False, epi, kc, vpt, True, tpw)
     k = body(asm, name)
     loads = [m.start() for m in re.finditer(r"global_load_dwordx4 .* nt$", k, flags=re.M)]
-    # each lane: tpw / 2 vectors of its token's row per slot
-    assert len(loads) == abs(kc) * (tpw // 2), len(loads)
+    # each lane: vpt vectors of its token's row per slot
+    assert len(loads) == abs(kc) * vpt, len(loads)
     first_wait = re.search(r"s_waitcnt vmcnt\(\d+\)", k)
     assert first_wait is None or first_wait.start() > loads[-1]
     # the per-token slot metadata stays in registers (an array the compiler
