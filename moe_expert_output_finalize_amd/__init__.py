@@ -335,14 +335,30 @@ def beam_moe_finalize_norm_residual_norm(
         post_weight: torch.Tensor | None, post_eps: float | None,
         next_weight: torch.Tensor | None, next_eps: float | None,
         scales: tuple[float, float] | None, routed_scale: float = 1.0, stream=None, *,
-        hidden_out: torch.Tensor | None = None, normalized_out: torch.Tensor | None = None):
+        hidden_out: torch.Tensor | None = None, normalized_out: torch.Tensor | None = None,
+        strategy: str | None = None):
     """Fused token-major finalize -> (post-norm) -> residual add -> next norm
     for residual.shape[0] tokens; returns (hidden, normalized or None).
 
     ``expert_outputs`` is [capacity, top_k, hidden] (the producer's
     [capacity * top_k, hidden] rows viewed per token).  ``hidden_out`` and
-    ``normalized_out`` may be given to write into existing tensors."""
+    ``normalized_out`` may be given to write into existing tensors.
+    ``strategy`` (the page's keyword of the same name, "vllm.models.beam.
+    nvidia.moe_finalize"): None or "fused" runs the fused kernel; "unfused"
+    runs beam_moe_finalize into a BF16 intermediate and then
+    beam_norm_residual_norm, the two-step reference kept for validation and
+    benchmarking (bit-identical results); anything else raises ValueError."""
     name = "beam_moe_finalize_norm_residual_norm"
+    if strategy not in (None, "fused", "unfused"):
+        raise ValueError(f"{name}: unknown strategy {strategy!r} (None, 'fused' or 'unfused')")
+    if strategy == "unfused":
+        T, hidden = _t(name, "residual", residual, torch.bfloat16, 2)
+        y = torch.empty((T, hidden), dtype=torch.bfloat16, device=residual.device)
+        beam_moe_finalize(expert_outputs, expert_weights, y, routed_scale, post_weight,
+                          post_eps, stream)
+        return beam_norm_residual_norm(y, residual, None, None, next_weight, next_eps, scales,
+                                       stream, hidden_out=hidden_out,
+                                       normalized_out=normalized_out)
     dev = _device(name, expert_outputs, expert_weights, residual, post_weight, next_weight,
                   hidden_out, normalized_out)
     capacity, top_k, hidden, wrows, T = _token_major(name, expert_outputs, expert_weights,

@@ -228,6 +228,19 @@ def test_binding_rejects_host_tensors():
                         torch.zeros(1, 256, dtype=torch.bfloat16))
 
 
+@pytest.mark.parametrize("strategy", ["oneshot", "twoshot", "FUSED", ""])
+def test_unknown_strategy_is_rejected(strategy):
+    """The fused residual entry point takes the page's strategy keyword: None,
+    "fused" or "unfused"; any other value raises ValueError before a tensor
+    is looked at (so host tensors suffice here)."""
+    import torch
+    e = torch.zeros(1, 1, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="strategy"):
+        mf.beam_moe_finalize_norm_residual_norm(e, torch.zeros(1, 1),
+                                                torch.zeros(1, 256, dtype=torch.bfloat16),
+                                                None, None, None, None, None, strategy=strategy)
+
+
 def test_c_driver_links_against_the_library():
     """The plain-C driver of the GPU tests resolves libmoe_finalize.so and the
     HIP runtime; without arguments it prints its usage before any HIP call."""

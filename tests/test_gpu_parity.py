@@ -444,6 +444,34 @@ def test_extreme_values_propagate_like_the_oracle():
                       "extreme rmsnorm (NaN/inf rows)")
 
 
+@pytest.mark.parametrize("post,post_w,nxt,next_w,scales", [
+    (True, True, True, True, (0.5, 2.0)), (False, False, True, False, None),
+    (True, False, False, False, (1.0, -1.0)),
+])
+def test_strategy_unfused_equals_fused(post, post_w, nxt, next_w, scales):
+    """The page's strategy keyword: "unfused" (finalize into a BF16
+    intermediate, then the consumer) and "fused" give the default fused
+    call's outputs bit for bit."""
+    c, res, nw, next_eps, scales = residual_case(77, 40, 6, 2048, 33, post, post_w, nxt, next_w,
+                                                 scales, 1.25)
+    d = TokenMajorOnDevice(c)
+    resd = dev_bf16(res)
+    nwd = None if nw is None else dev_bf16(nw)
+    outs = {}
+    for strategy in (None, "fused", "unfused"):
+        outs[strategy] = mf.beam_moe_finalize_norm_residual_norm(
+            d.expert_outputs, d.weights, resd, d.post_weight, c.post_eps, nwd, next_eps, scales,
+            c.routed_scale, strategy=strategy)
+    sync()
+    h0, n0 = outs[None]
+    for strategy in ("fused", "unfused"):
+        h, n = outs[strategy]
+        assert_bits_equal(host_bits(h), host_bits(h0), f"{strategy} hidden")
+        assert (n is None) == (n0 is None)
+        if n is not None:
+            assert_bits_equal(host_bits(n), host_bits(n0), f"{strategy} normalized")
+
+
 def test_hardware_bf16_rounding_matches_round_to_nearest_even():
     """K = 1 and rows of 1.0 make the output bf16(weight): the packed convert
     is checked on ties, subnormals, overflow and NaN against the oracle's
