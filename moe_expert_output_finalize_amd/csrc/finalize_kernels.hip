@@ -93,6 +93,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// sx * y + sr * r rounded once to BF16 (by pack_bf16x2), returned as the
+// FP32 value to pack.  Each product of an FP32 scale and a BF16 value has at
+// most 32 significant bits, so both are exact in binary64 and the fused
+// multiply-add rounds their sum once; that binary64 sum is then rounded to
+// FP32 to odd (an inexact result keeps its last bit set), which has 16 bits
+// more than BF16, so the final round to nearest even sees no false tie and
+// gives the BF16 rounding of the binary64 sum.  FP32 arithmetic instead
+// (a multiply, a fused multiply-add, then BF16) rounds up to three times.
+__device__ __forceinline__ float affine_to_odd(float sx, float y, float sr, float r)
+{
+    const double d = __builtin_fma((double)sx, (double)y, (double)sr * (double)r);
+    const float f = (float)d;
+    const uint32_t b = __float_as_uint(f);
+    if ((double)f == d || f != f || (b & 1u))
+        return f;
+    // inexact and even: the neighbour on d's side (0 moves to the smallest
+    // subnormal of its sign, infinity back to the largest finite value)
+    return __uint_as_float(__builtin_fabs(d) > __builtin_fabs((double)f) ? b + 1u : b - 1u);
+}
+
 // ------------------------------------------------------------ memory -----
 
 __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
@@ -154,32 +174,26 @@ __device__ __forceinline__ float dpp_mov(float v)
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// Value of lane `l` (a constant) of v, as a wave-uniform scalar.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_value(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // Sum of v over the workgroup, returned to every thread.  All threads of the
 // workgroup must call it (it contains a barrier when there are several waves).
 // Two sums in one kernel use different banks, so the second's LDS writes
-// cannot overtake a slower wave's reads of the first.  TPW > 1: a one-wave
-// workgroup holding TPW tokens of 64 / TPW lanes each, and every lane gets
-// its own token's sum: with 8 or 4 tokens, the 8- or 16-lane sum every lane
-// holds after the DPP steps.
-template <int TPW = 1>
+// cannot overtake a slower wave's reads of the first.  Within a wave the sum
+// is the 16-lane DPP butterfly of each row (all 16 lanes end with the same
+// bits), then the four rows in order.
 __device__ __forceinline__ float block_sum(float v, int bank = 0)
 {
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
     v += dpp_mov<0x141>(v);   // row_half_mirror: 8-lane sums
-    if constexpr (TPW == 8)
-        return v;
     v += dpp_mov<0x140>(v);   // row_mirror: 16-lane sums
-    if constexpr (TPW == 4)
-        return v;
     const int iv = __builtin_bit_cast(int, v);
-    if constexpr (TPW == 2) {
-        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
-                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
-        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
-                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
-        return (threadIdx.x & 32) ? hi : lo;
-    }
     float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
               __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16)) +
               __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
@@ -197,13 +211,71 @@ __device__ __forceinline__ float block_sum(float v, int bank = 0)
     return s;
 }
 
-
-// Value of lane `l` (a constant) of v, as a wave-uniform scalar.
-__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ __forceinline__ float lane_value(float v, int l)
+// Sum of the squares of acc over this lane's token's row.  One token per
+// workgroup: each lane's FMA chain over its vectors, then block_sum.
+// TPW > 1 tokens per wave (hidden 256 and 512): the order is that of one
+// token per wave at these sizes, where lane l holds vector l: each vector's
+// 8 squares by an FMA chain, each block of 16 vectors by the 16-lane DPP
+// butterfly, then the blocks in order, ((B0 + B1) + B2) + B3.  A lane here
+// holds vector l % LPT + LPT i of its token (LPT = 64 / TPW lanes per
+// token): with 16 lanes, vector i is block i; with 32, block 2i in the
+// token's first row of lanes and 2i + 1 in its second; with 8, half of
+// block i / 2, whose halves the butterfly's last step adds.  So kernels of
+// different layouts over the same rows, such as the fused residual path and
+// its standalone consumer, compute the same sum bit for bit.
+template <int VPT, int TPW>
+__device__ __forceinline__ float row_sum_sq(const float (&acc)[VPT][8], int bank = 0)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    if constexpr (TPW == 1) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);   // idle vectors hold 0
+        return block_sum(ss, bank);
+    } else {
+        float r[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            float v = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v = __builtin_fmaf(acc[i][e], acc[i][e], v);
+            v += dpp_mov<0xB1>(v);
+            v += dpp_mov<0x4E>(v);
+            v += dpp_mov<0x141>(v);
+            if constexpr (TPW != 8)
+                v += dpp_mov<0x140>(v);
+            r[i] = v;
+        }
+        if constexpr (TPW == 8) {
+            static_assert(VPT % 2 == 0, "two 8-vector halves per block");
+            float s = r[0] + r[1];
+#pragma unroll
+            for (int b = 1; b < VPT / 2; ++b)
+                s += r[2 * b] + r[2 * b + 1];
+            return s;
+        } else if constexpr (TPW == 4) {
+            float s = r[0];
+#pragma unroll
+            for (int i = 1; i < VPT; ++i)
+                s += r[i];
+            return s;
+        } else {
+            static_assert(TPW == 2, "2, 4 or 8 tokens per wave");
+            float lo = lane_value(r[0], 0) + lane_value(r[0], 16);
+            float hi = lane_value(r[0], 32) + lane_value(r[0], 48);
+#pragma unroll
+            for (int i = 1; i < VPT; ++i) {
+                lo = (lo + lane_value(r[i], 0)) + lane_value(r[i], 16);
+                hi = (hi + lane_value(r[i], 32)) + lane_value(r[i], 48);
+            }
+            return (threadIdx.x & 32) ? hi : lo;
+        }
+    }
 }
+
 
 // ------------------------------------------------------------ kernel -----
 
@@ -271,13 +343,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
     if constexpr (EPI == Epilogue::kResidualNorm) {
         // Optional post-norm of s, rounded to BF16.
         if (a.has_post) {
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < VPT; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-            ss = block_sum<TPW>(ss, 0);
+            const float ss = row_sum_sq<VPT, TPW>(acc, 0);
             const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
             for (int i = 0; i < VPT; ++i)
@@ -293,16 +359,17 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                     acc[i][2 * q + 1] = bf16_hi(p);
                 }
         }
-        // hidden = bf16(scale_x * y + scale_res * residual), kept widened in acc.
+        // hidden = bf16(scale_x * y + scale_res * residual), one rounding,
+        // kept widened in acc.
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             u32x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float h0 = __builtin_fmaf(a.scale_x, acc[i][2 * q],
-                                                a.scale_res * elem(rv[i], 2 * q));
-                const float h1 = __builtin_fmaf(a.scale_x, acc[i][2 * q + 1],
-                                                a.scale_res * elem(rv[i], 2 * q + 1));
+                const float h0 = affine_to_odd(a.scale_x, acc[i][2 * q], a.scale_res,
+                                               elem(rv[i], 2 * q));
+                const float h1 = affine_to_odd(a.scale_x, acc[i][2 * q + 1], a.scale_res,
+                                               elem(rv[i], 2 * q + 1));
                 const uint32_t p = pack_bf16x2(h0, h1);
                 o[q] = p;
                 acc[i][2 * q] = bf16_lo(p);
@@ -322,13 +389,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                 nv2[i] = EXACT ? reinterpret_cast<const u32x4 *>(a.gain2)[j]
                                : load_vec_bounded<0>(a.gain2, nv, j);
         }
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);
-        ss = block_sum<TPW>(ss, 1);
+        const float ss = row_sum_sq<VPT, TPW>(acc, 1);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps2);
         const __amdgpu_buffer_rsrc_t out2_row =
             row_resource(a.out2 + t_row * (int64_t)a.hidden, (uint32_t)out_nv * 16u);
@@ -368,13 +429,7 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                 for (int e = 0; e < 8; ++e)
                     acc[i][e] *= g[i][e];
         }
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ss = __builtin_fmaf(acc[i][e], acc[i][e], ss);   // idle vectors hold 0
-        ss = block_sum<TPW>(ss);
+        const float ss = row_sum_sq<VPT, TPW>(acc);
         const float inv = rsqrtf(ss / (float)a.hidden + a.eps);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {

@@ -11,6 +11,9 @@ next norm options of the residual path.  Sizes are bounded so that the
 oracle finishes a case in a fraction of a second; every case has at least
 4096 output elements so that the bit-exact share floors mean something.
 
+A second family draws small rows (hidden 256 and 512, top-k up to 8) with
+up to 3000 tokens.
+
 The bar is the fixed cases' bar: outputs without a norm are bit-exact,
 normalised outputs within 1 BF16 ulp of the oracle.
 """
@@ -33,16 +36,24 @@ pytestmark = pytest.mark.gpu
 
 KINDS = ("index_map", "token_major", "residual", "standalone")
 N_CASES = 64
+N_SMALL_CASES = 32
 MAX_GATHERED = 3_000_000          # gathered row elements per case
 MIN_OUTPUT = 4096                 # output elements per case
 INT32_MIN, INT32_MAX = int(np.iinfo(np.int32).min), int(np.iinfo(np.int32).max)
 
 
-def draw_shape(rng, top_k_max=32):
-    hidden = 256 * int(rng.integers(1, 33))
-    top_k = int(rng.integers(1, top_k_max + 1))
+def draw_shape(rng, top_k_max=32, small=False):
+    """(hidden, top-k, tokens).  small: hidden 256 or 512 at top-k up to 8,
+    where one wave holds several tokens, with up to 3000 tokens so that the
+    grid spans full runs of workgroups per XCD."""
+    if small:
+        hidden = 256 * int(rng.integers(1, 3))
+        top_k = int(rng.integers(1, min(top_k_max, 8) + 1))
+    else:
+        hidden = 256 * int(rng.integers(1, 33))
+        top_k = int(rng.integers(1, top_k_max + 1))
     t_min = math.ceil(MIN_OUTPUT / hidden)
-    t_max = max(t_min, min(300, MAX_GATHERED // (top_k * hidden)))
+    t_max = max(t_min, min(3000 if small else 300, MAX_GATHERED // (top_k * hidden)))
     return hidden, top_k, int(rng.integers(t_min, t_max + 1))
 
 
@@ -61,8 +72,8 @@ def describe(**kw) -> str:
     return " ".join(f"{k}={v}" for k, v in kw.items())
 
 
-def run_index_map(seed, rng):
-    H, K, T = draw_shape(rng)
+def run_index_map(seed, rng, small=False):
+    H, K, T = draw_shape(rng, small=small)
     R = T * K + int(rng.integers(0, 64))
     S = H + 8 * int(rng.integers(0, 17))
     wdt = str(rng.choice(["fp32", "bf16"]))
@@ -102,8 +113,8 @@ def run_index_map(seed, rng):
     assert_within_ulp(host_bits(out), want_n, 1, NORM_MIN_EXACT, f"unfused norm {what}")
 
 
-def run_token_major(seed, rng):
-    H, K, T = draw_shape(rng)
+def run_token_major(seed, rng, small=False):
+    H, K, T = draw_shape(rng, small=small)
     cap = T + int(rng.integers(0, 5))
     norm = bool(rng.random() < 0.6)
     pw = (0.05 if rng.random() < 0.5 else None) if norm else None
@@ -127,8 +138,8 @@ def run_token_major(seed, rng):
         assert_bits_equal(got, want, what)
 
 
-def run_residual(seed, rng):
-    H, K, T = draw_shape(rng)
+def run_residual(seed, rng, small=False):
+    H, K, T = draw_shape(rng, small=small)
     post = bool(rng.integers(0, 2))
     post_w = post and bool(rng.integers(0, 2))
     nxt = bool(rng.random() < 0.75)
@@ -143,9 +154,9 @@ def run_residual(seed, rng):
     check_residual(*args, what)
 
 
-def run_standalone(seed, rng):
+def run_standalone(seed, rng, small=False):
     """mf_rmsnorm and the residual consumer (no post-norm) on strided rows."""
-    H, _, T = draw_shape(rng, top_k_max=1)
+    H, _, T = draw_shape(rng, top_k_max=1, small=small)
     S = H + 8 * int(rng.integers(0, 17))
     wbn = bool(rng.integers(0, 2))
     gc = float(rng.choice([1.0, 0.0, -0.5]))
@@ -171,7 +182,7 @@ def run_standalone(seed, rng):
     assert_within_ulp(host_bits(out), want, 1, NORM_MIN_EXACT, f"mf_rmsnorm {what}")
     wh, wn = oracle.beam_norm_residual_norm(x, res, None, None, nw if next_w else None, eps,
                                             scales)
-    assert_within_ulp(host_bits(h), wh, 1, 0.999, f"consumer hidden {what}")
+    assert_bits_equal(host_bits(h), wh, f"consumer hidden {what}")
     assert_within_ulp(host_bits(n), wn, 1, NORM_MIN_EXACT, f"consumer normalized {what}")
 
 
@@ -184,3 +195,13 @@ def test_random_case(seed):
     kind = KINDS[seed % len(KINDS)]
     rng = np.random.Generator(np.random.PCG64(40_000 + seed))
     RUNNERS[kind](seed, rng)
+
+
+# Small rows (hidden 256 and 512, top-k up to 8): the kernels that hold
+# several tokens per wave, and beside them the one-token kernels of the same
+# hidden sizes.
+@pytest.mark.parametrize("seed", range(N_SMALL_CASES))
+def test_random_small_row_case(seed):
+    kind = KINDS[seed % len(KINDS)]
+    rng = np.random.Generator(np.random.PCG64(90_000 + seed))
+    RUNNERS[kind](1000 + seed, rng, small=True)
