@@ -360,23 +360,32 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
                 }
         }
         // hidden = bf16(scale_x * y + scale_res * residual), one rounding,
-        // kept widened in acc.
+        // kept widened in acc.  With scales of +-1 (the default pair (1, 1))
+        // the FP32 sum of the two BF16 values is already that rounding: it
+        // is exact unless their exponents differ by more than 16, and then
+        // both it and the exact sum round to the larger value; other scales
+        // take affine_to_odd.  The branch is uniform.
+        auto add_residual = [&](auto sum) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            u32x4 o;
+            for (int i = 0; i < VPT; ++i) {
+                u32x4 o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float h0 = affine_to_odd(a.scale_x, acc[i][2 * q], a.scale_res,
-                                               elem(rv[i], 2 * q));
-                const float h1 = affine_to_odd(a.scale_x, acc[i][2 * q + 1], a.scale_res,
-                                               elem(rv[i], 2 * q + 1));
-                const uint32_t p = pack_bf16x2(h0, h1);
-                o[q] = p;
-                acc[i][2 * q] = bf16_lo(p);
-                acc[i][2 * q + 1] = bf16_hi(p);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t p = pack_bf16x2(sum(acc[i][2 * q], elem(rv[i], 2 * q)),
+                                                   sum(acc[i][2 * q + 1], elem(rv[i], 2 * q + 1)));
+                    o[q] = p;
+                    acc[i][2 * q] = bf16_lo(p);
+                    acc[i][2 * q + 1] = bf16_hi(p);
+                }
+                store(i, o);
             }
-            store(i, o);
-        }
+        };
+        const bool unit_scales = (a.scale_x == 1.0f || a.scale_x == -1.0f) &&
+                                 (a.scale_res == 1.0f || a.scale_res == -1.0f);
+        if (unit_scales)
+            add_residual([&](float y, float r) { return __builtin_fmaf(a.scale_x, y, a.scale_res * r); });
+        else
+            add_residual([&](float y, float r) { return affine_to_odd(a.scale_x, y, a.scale_res, r); });
         if (!a.has_next)
             return;
         // normalized = bf16(hidden * inv_rms(hidden) * next_weight)
