@@ -36,7 +36,7 @@ pytestmark = pytest.mark.gpu
 
 KINDS = ("index_map", "token_major", "residual", "standalone")
 N_CASES = 64
-N_SMALL_CASES = 32
+N_SMALL_CASES = 64
 MAX_GATHERED = 3_000_000          # gathered row elements per case
 MIN_OUTPUT = 4096                 # output elements per case
 INT32_MIN, INT32_MAX = int(np.iinfo(np.int32).min), int(np.iinfo(np.int32).max)
