@@ -458,7 +458,8 @@ __device__ __forceinline__ void finish_token(float (&acc)[VPT][8], const u32x4 (
     }
 }
 
-// One workgroup finalizes token a.token_base + blockIdx.x.
+// One workgroup finalizes token a.token_base + blockIdx.x (TPW > 1: the
+// TPW tokens of a token block, described below).
 //   L      where slot rows come from (index map, token major, one row per token)
 //   W_BF16 weights are BF16 (else FP32)
 //   EPI    what follows the FP32 routed sum
